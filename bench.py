@@ -1,0 +1,234 @@
+"""Benchmark of the predictor-gated sparse FFN decode step on one MI355X.
+
+One step = one pass of the whole hot path over one token batch: predictor
+(both layers, threshold, union) with the compaction fused into its last
+workgroup, then the sparse FFN over the hot and the cold partition with the
+merge fused into the down projection's reduction.
+
+Default workload: the OPT-30B-shaped ReLU layer (d_model 7168, d_ffn 28672,
+predictor rank 1024, fp16 weights, fp32 accumulation, batch 1), hot partition
+= top 26% of neurons by activation count over 1024 profiling samples (profiled,
+indexed and permuted on the GPU before timing).  Steps rotate over INSTANCES
+device copies of the layer (same values, distinct addresses) with a fresh
+seeded x per step, so the 256 MB Infinity Cache cannot serve the weights.
+
+Reported: mean microseconds per layer step (`value`), achieved GB/s on the
+bytes the step must touch, per-kernel durations from HIP events recorded at
+each kernel's own dispatch, the dense FFN of the same layer, and the CPU
+oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("sparse-FFN µs/layer + achieved HBM GB/s on touched weights vs peak, batch 1")
+PEAK_HBM_GBPS = 8000.0
+INSTANCES = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def esize(dt):
+    return {"f32": 4, "f16": 2}[dt]
+
+
+def wrow_bytes(wl):
+    return wl.d // 2 + wl.d // 16 if wl.wdtype == "q4_0" else wl.d * esize(wl.wdtype)
+
+
+def kernel_bytes(wl, B, active, nch):
+    """Algorithmic bytes per launch of each kernel for one step with `active` neurons."""
+    ep = esize(wl.pdtype)
+    ex = esize(wl.xdtype)
+    m_up = 2 if wl.act == "reglu" else 1
+    return {
+        "k_pred_l1": wl.r * wl.d * ep + B * wl.d * ex + B * wl.r * 4,
+        "k_pred_l2": wl.n * wl.r * ep + 4 * wl.n + B * wl.r * 4 + wl.n // 8 + 4 * active,
+        "k_up": active * (m_up * wrow_bytes(wl) + 4 + 4) + B * wl.d * ex + 4 * B * active,
+        "k_down": active * (wrow_bytes(wl) + 4) + 4 * B * active + 4 * B * wl.d,
+    }
+
+
+def step_bytes(wl, B, active):
+    """Bytes one layer step must touch: predictor weights + b2, the active rows of the FFN
+    (W_up / W_gate / W_downT rows and the fp32 bias), x in, y out."""
+    m = 3 if wl.act == "reglu" else 2
+    pred = (wl.d * wl.r + wl.r * wl.n) * esize(wl.pdtype) + 4 * wl.n
+    return pred + active * (m * wrow_bytes(wl) + 4) + B * wl.d * esize(wl.xdtype) + 4 * B * wl.d
+
+
+def cpu_baseline(wl, L, n_hot, B, budget_s=12.0):
+    """The oracle's layer step (predict, compact, sparse FFN per partition, merge) on the host."""
+    from oracle import oracle as O
+    from workload import synth as S
+    hot = O.Part.from_layer(L, 0, n_hot)
+    cold = O.Part.from_layer(L, n_hot, wl.n) if n_hot < wl.n else None
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        x = S.make_x(wl, 0, 10_000 + steps, B)
+        O.layer_step(L.P1t, L.P2t, L.b2, L.threshold, hot, cold, x)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 200:
+            break
+    return {"value": round(el / steps * 1e6, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} layer steps of the same {wl.name} layer (batch {B}), "
+                      f"single-threaded C oracle, fp64 accumulation"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="opt30b-fp16")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--instances", type=int, default=INSTANCES)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the sparse FFN is a single-GPU path here "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_activation_ffn_amd import binding as pb
+    from sparse_activation_ffn_amd.layer import DeviceLayer, StepBuffers
+    from workload import synth as S
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = S.WORKLOADS[args.workload]
+    B = args.batch
+    K, W = args.steps, args.warmup
+    log(f"[bench] generating {wl.name} layer ...")
+    L = S.make_layer(wl)
+    base = DeviceLayer.upload(L, dev)
+    n_hot = wl.n
+    perm_np = None
+    if wl.hot_frac is not None:
+        log("[bench] profiling + neuron index on the GPU ...")
+        X = torch.from_numpy(S.make_profile_x(wl, 0)).to(dev)
+        counts = base.profile_counts(X)
+        perm, n_hot = base.build_index(counts, S.budget_bytes(wl), S.bytes_per_neuron(wl))
+        base.apply_index(perm, n_hot)
+        perm_np = perm.cpu().numpy()
+        del X
+    layers = [base] + [base.clone() for _ in range(args.instances - 1)]
+    descs = [(ly.predictor(), ly.parts()) for ly in layers]
+    buf = StepBuffers(base, B, dev)
+    xs = [torch.from_numpy(S.make_x(wl, 0, s, B)).to(dev) for s in range(W + K)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        pred, (hot, cold) = descs[i % len(layers)]
+        x = xs[i]
+        pb.pi_predict(pred, x, buf.mask, None, buf.lists, buf.ws)
+        pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, None, None, buf.y, buf.ws)
+
+    log(f"[bench] warmup {W} + timed {K} steps over {len(layers)} instances ...")
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(W, W + K):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    us_step = ms_total * 1e3 / K
+
+    # second pass over the same steps: per-kernel durations from dispatch events, and the
+    # active count of each step (deterministic, so identical to the first pass)
+    kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2, "k_up": pb.PI_K_UP,
+            "k_down": pb.PI_K_DOWN}
+    for kid in kids.values():
+        pb.pi_kernel_timer_start(kid, K)
+    active = []
+    hot_active = []
+    for i in range(W, W + K):
+        step(i)
+        c = buf.counts.cpu().numpy()
+        active.append(int(c[0] + c[1]))
+        hot_active.append(int(c[0]))
+    kern_ms = {name: pb.pi_kernel_timer_stop(kid) for name, kid in kids.items()}
+    kern_us = {name: ms * 1e3 / max(k, 1) for name, (ms, k) in kern_ms.items()}
+    mean_active = float(np.mean(active))
+    nch_est = None
+    kb = [kernel_bytes(wl, B, a, nch_est) for a in active]
+    kb_mean = {k: float(np.mean([b[k] for b in kb])) for k in kb[0]}
+    touched = float(np.mean([step_bytes(wl, B, a) for a in active]))
+    gbps_touched = touched / (us_step * 1e-6) / 1e9
+    dom = max(kern_us, key=kern_us.get)
+    dom_gbps = kb_mean[dom] / (kern_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
+                "traffic": None}
+
+    dense = None
+    if not args.no_dense:
+        yd = torch.empty((B, wl.d), dtype=torch.float32, device=dev)
+        parts = [ly.part() for ly in layers]
+        for i in range(3):
+            pb.pi_dense_ffn(parts[i % len(parts)], xs[i], yd, buf.ws)
+        torch.cuda.synchronize()
+        KD = max(10, K // 10)
+        e0.record()
+        for i in range(KD):
+            pb.pi_dense_ffn(parts[i % len(parts)], xs[i], yd, buf.ws)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_us = e0.elapsed_time(e1) * 1e3 / KD
+        dense_bytes = 2 * wl.n * wrow_bytes(wl) + 4 * wl.n
+        dense = {"us": round(dense_us, 2), "gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+                 "speedup_sparse_step_vs_dense_ffn": round(dense_us / us_step, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        Lh = L
+        if perm_np is not None:
+            import dataclasses
+            take = lambda a: None if a is None else np.ascontiguousarray(a[perm_np])  # noqa: E731
+            Lh = dataclasses.replace(L, W_up=take(L.W_up), W_gate=take(L.W_gate),
+                                     W_downT=take(L.W_downT), b_up=take(L.b_up),
+                                     b_gate=take(L.b_gate), P2t=take(L.P2t), b2=take(L.b2))
+        cpu = cpu_baseline(wl, Lh, n_hot, B)
+
+    out = {
+        "metric": METRIC, "value": round(us_step, 3), "unit": "us/layer", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "d_model": wl.d, "d_ffn": wl.n, "predictor_rank": wl.r,
+                   "batch": B, "weights": wl.wdtype, "accumulate": "f32",
+                   "hot_fraction": wl.hot_frac, "n_hot": n_hot, "instances": len(layers),
+                   "mean_active": round(mean_active, 1),
+                   "mean_hot_active": round(float(np.mean(hot_active)), 1)},
+        "touched_bytes_per_step": round(touched),
+        "achieved_gbps_touched": round(gbps_touched, 1),
+        "frac_of_peak_touched": round(gbps_touched / PEAK_HBM_GBPS, 4),
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "kernel_bytes": {k: round(v) for k, v in kb_mean.items()},
+        "roofline": roofline, "dense_ffn": dense, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

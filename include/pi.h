@@ -1,0 +1,263 @@
+/*
+ * pi.h -- C ABI of the predictor-gated, neuron-aware sparse FFN for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (PowerInfer pages):
+ *  - chatpaper.ai abstract; CSDN article, section on sparse activation: a
+ *    small per-layer predictor names the FFN neurons an input will activate,
+ *    and neuron-aware sparse operators compute only those neurons.
+ *  - CSDN article, section on the CPU/GPU hybrid design and its figure: each
+ *    memory partition ("hot" and "cold") computes the predicted neurons it
+ *    holds; the partial results are merged.
+ *  - CSDN article, overall-architecture section; hada.io README summary
+ *    (--vram-budget, GPU index): an offline step profiles activation
+ *    frequencies and places the most frequently active neurons in the fast
+ *    partition under a memory budget.
+ *  - hada.io README summary, quantisation section: INT4 weights in Q4_0.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller unless marked
+ *    [host].  The library never allocates, frees or retains caller memory.
+ *  - Every call only enqueues work on `stream` (a hipStream_t passed as
+ *    void*, NULL = the default stream) and returns; no call synchronises
+ *    the host except pi_kernel_timer_stop.
+ *  - Arguments are validated before anything is enqueued; on an error the
+ *    call enqueues nothing and returns a nonzero pi_status.  pi_last_error()
+ *    then holds a message (thread-local).
+ *  - Weight, input and output tensors must be 16-byte aligned; index lists,
+ *    counts and masks 8-byte aligned.
+ *  - Layout: one neuron owns one row.  W_up, W_gate and W_downT (the
+ *    transpose of W_down) are [rows][d] row-major; P1t is [r][d]; P2t is
+ *    [n][r]; biases are float32 [rows].  x is [B][d].
+ *  - A Q4_0 row of d elements (d % 256 == 0) is d/2 code bytes followed by
+ *    d/32 fp16 scales (9d/16 bytes).  Code byte 16*j + t (t < 16) holds
+ *    element 32*j + t in its low nibble and element 32*j + t + 16 in its
+ *    high nibble; element value = (code - 8) * scale_j.
+ *  - Calls on one stream run in order.  Two calls that share a workspace
+ *    must not run concurrently (on different streams).
+ */
+#ifndef PI_H
+#define PI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pi_status;
+enum {
+    PI_OK = 0,
+    PI_ERR_ARG = 1,        /* NULL where a tensor is required, bad enum, bad option */
+    PI_ERR_SHAPE = 2,      /* a size out of range or not a multiple the layout needs */
+    PI_ERR_ALIGN = 3,      /* a pointer misaligned for its role */
+    PI_ERR_DTYPE = 4,      /* unsupported dtype combination */
+    PI_ERR_WORKSPACE = 5,  /* workspace missing or smaller than pi_workspace_bytes() */
+    PI_ERR_BUDGET = 6,     /* negative budget or non-positive bytes per neuron */
+    PI_ERR_HIP = 7         /* the HIP runtime reported an error while enqueueing */
+};
+
+/* element storage types */
+enum { PI_F32 = 0, PI_F16 = 1, PI_Q4_0 = 2 };
+/* FFN activations (hada.io README summary: ReLU and ReGLU models) */
+enum { PI_RELU = 0, PI_REGLU = 1 };
+
+/* Largest batch a call accepts. */
+#define PI_MAX_BATCH 64
+
+/*
+ * Low-rank activation predictor of one layer (CSDN article, section on
+ * sparse activation):
+ *   u[b][j]     = max(0, sum_k P1t[j][k] * x[b][k])        j < r
+ *   logit[b][i] = sum_j P2t[i][j] * u[b][j] + b2[i]        i < n
+ *   active(i)   = OR over tokens b of (logit[b][i] > threshold)
+ * u and logits are float32 (never rounded to a narrower type).
+ */
+typedef struct pi_predictor {
+    int32_t d;            /* model width, d % 64 == 0 */
+    int32_t n;            /* neurons, n >= 1 */
+    int32_t r;            /* predictor rank, r % 16 == 0 */
+    int32_t wdtype;       /* PI_F32 or PI_F16 for P1t and P2t */
+    const void* P1t;      /* [r][d] */
+    const void* P2t;      /* [n][r] */
+    const float* b2;      /* [n] or NULL (zeros) */
+    float threshold;      /* strict: logit > threshold is active */
+} pi_predictor;
+
+/*
+ * A partition (a contiguous block of rows of the neuron-permuted layer) of a
+ * ReLU or ReGLU FFN layer.  Per token b and listed neuron i:
+ *   ReLU : h = max(0, W_up[i].x_b + b_up[i])
+ *   ReGLU: h = max(0, W_gate[i].x_b + b_gate[i]) * (W_up[i].x_b + b_up[i])
+ *   y_b += h * W_downT[i][:]
+ * NULL biases are zeros; there is no down-projection bias.
+ */
+typedef struct pi_ffn_part {
+    int32_t d;            /* model width: d % 64 == 0 (d % 256 == 0 for Q4_0) */
+    int32_t rows;         /* neurons in this partition, >= 0 */
+    int32_t wdtype;       /* PI_F32, PI_F16 or PI_Q4_0 (all three matrices) */
+    int32_t act;          /* PI_RELU or PI_REGLU */
+    const void* W_up;     /* [rows][d] */
+    const void* W_gate;   /* [rows][d], required for PI_REGLU, ignored for PI_RELU */
+    const float* b_up;    /* [rows] or NULL */
+    const float* b_gate;  /* [rows] or NULL */
+    const void* W_downT;  /* [rows][d] */
+} pi_ffn_part;
+
+/*
+ * Active-neuron lists split at n_hot (CSDN article, hybrid-design figure:
+ * the predicted ids go to the partition that holds them).  Ids are in the
+ * permuted layer: hot ids are < n_hot, cold ids are stored minus n_hot.
+ * Both lists are ascending; counts[0] = hot count, counts[1] = cold count
+ * (device memory, so no host round trip is needed between calls).
+ */
+typedef struct pi_active_lists {
+    int32_t n_hot;        /* 0 <= n_hot <= n */
+    int32_t* hot_idx;     /* [n_hot] capacity */
+    int32_t* cold_idx;    /* [n - n_hot] capacity; may be NULL iff n_hot == n */
+    int32_t* counts;      /* [2] */
+} pi_active_lists;
+
+/*
+ * Workspace bytes that suffice for every call below on a layer with these
+ * sizes and any batch up to B (d model width, n neurons, r predictor rank).
+ * Returns 0 if the sizes are out of range.
+ */
+size_t pi_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t B);
+
+/*
+ * Zero-fills a workspace (with a fill kernel).  A workspace must be zeroed
+ * once before its first use; every call leaves its synchronisation counters
+ * at zero again, so it need not be re-zeroed between calls.
+ */
+pi_status pi_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Predicts the active neurons of one layer for the B tokens of x [B][d]
+ * (xdtype PI_F32 or PI_F16).
+ *   mask   [ceil(n/64)] uint64, out: bit i % 64 of word i / 64 is set iff
+ *          neuron i is active for some token; bits >= n are 0.
+ *   logits [B][n] float32, out, or NULL.
+ *   lists  optional: if not NULL, the same call also compacts the mask into
+ *          ascending hot/cold lists (as pi_compact_active does), fused into
+ *          the predictor's last workgroup.
+ * Needs a workspace (pi_workspace_bytes).
+ */
+pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xdtype,
+                     uint64_t* mask, float* logits, const pi_active_lists* lists,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Compacts mask [ceil(n/64)] into the ascending active lists of `lists`
+ * (one workgroup; no workspace).
+ */
+pi_status pi_compact_active(const uint64_t* mask, int32_t n, const pi_active_lists* lists,
+                            void* stream);
+
+/*
+ * Sparse FFN over one partition: y [B][d] float32 (overwritten) =
+ * sum over the first *count entries of idx (ascending ids < part->rows) of
+ * h_i * W_downT[i][:].  `count` is a device int32 scalar.
+ */
+pi_status pi_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                        const int32_t* idx, const int32_t* count, float* y,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse FFN over the hot and the cold partition in one pass, with the merge
+ * fused: y_hot and y_cold receive the two partial outputs (each may be NULL),
+ * y receives y_hot + y_cold (may be NULL).  `lists` comes from pi_predict or
+ * pi_compact_active with lists->n_hot == hot->rows.  cold may be NULL (or
+ * have 0 rows) when there is no cold partition.  Both partitions need the
+ * same d, wdtype and act.
+ */
+pi_status pi_sparse_ffn_split(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                              int32_t B, int32_t xdtype, const pi_active_lists* lists,
+                              float* y_hot, float* y_cold, float* y,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Merge of two partial outputs (CSDN article, hybrid-design figure: the
+ * partitions' results are combined on the GPU): y = y_hot + y_cold, [B][d]
+ * float32; y_cold NULL means zeros; y may alias y_hot or y_cold.
+ */
+pi_status pi_merge(const float* y_hot, const float* y_cold, int32_t B, int32_t d, float* y,
+                   void* stream);
+
+/*
+ * Dense FFN of one partition (every row computed): the measurement baseline
+ * the sparse path is compared with (hada.io README summary: dense inference
+ * mode).  y [B][d] float32, overwritten.
+ */
+pi_status pi_dense_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                       float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Offline activation profiling (CSDN article, overall-architecture section:
+ * activations are recorded over a general dataset).  counts [part->rows]
+ * uint32, overwritten: number of samples s of X [S][d] whose deciding
+ * pre-activation (W_up + b_up for ReLU, W_gate + b_gate for ReGLU) is > 0,
+ * decided in float32.
+ */
+pi_status pi_profile_counts(const pi_ffn_part* part, const void* X, int32_t S, int32_t xdtype,
+                            uint32_t* counts, void* stream);
+
+/*
+ * Neuron index under a memory budget (CSDN article, overall-architecture
+ * section; hada.io README summary, --vram-budget / GPU index):
+ *   perm [n] int32 device, out: perm[slot] = original neuron id, slots in
+ *        order of (counts desc, id asc);
+ *   n_hot [host] out: min(n, floor(budget_bytes / bytes_per_neuron)).
+ * counts [n] uint32 device.  The hot partition is slots [0, n_hot).
+ */
+pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budget_bytes,
+                                int64_t bytes_per_neuron, int32_t* perm, int32_t* n_hot,
+                                void* stream);
+
+/*
+ * Applies a neuron index to one per-neuron tensor: dst row s = src row
+ * perm[s], rows of row_bytes bytes (row_bytes % 4 == 0), s < rows.  src and
+ * dst must not overlap.
+ */
+pi_status pi_permute_rows(const void* src, void* dst, const int32_t* perm, int32_t rows,
+                          int64_t row_bytes, void* stream);
+
+/*
+ * Plain device copy of `bytes` bytes (bytes % 16 == 0): the reference
+ * kernel whose hardware byte counters calibrate traffic measurements.
+ */
+pi_status pi_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* Kernel ids for the timing hooks below. */
+enum {
+    PI_K_PRED_L1 = 0,     /* predictor first layer */
+    PI_K_PRED_L2 = 1,     /* predictor second layer + threshold + union (+ compaction) */
+    PI_K_COMPACT = 2,     /* standalone compaction */
+    PI_K_UP = 3,          /* gathered-row up/gate + activation */
+    PI_K_DOWN = 4,        /* column-scatter down + reduction + merge */
+    PI_K_MERGE = 5,       /* standalone merge */
+    PI_K_PROFILE = 6,
+    PI_K_INDEX = 7,
+    PI_K_COPY = 8,
+    PI_K_COUNT = 9
+};
+
+/*
+ * Timing hooks (measurement only).  After pi_kernel_timer_start(kid, max),
+ * the next `max` launches of kernel kid made by this host thread carry HIP
+ * start/stop events taken at the kernel's own dispatch and completion.
+ * pi_kernel_timer_stop synchronises those events and returns the summed
+ * duration in milliseconds and the number of timed launches [host].
+ */
+pi_status pi_kernel_timer_start(int32_t kid, int32_t max_launches);
+pi_status pi_kernel_timer_stop(int32_t kid, float* total_ms, int32_t* launches);
+const char* pi_kernel_name(int32_t kid);
+
+const char* pi_status_string(pi_status s);
+const char* pi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PI_H */

@@ -1,0 +1,46 @@
+"""Builds libpi.so (the HIP kernels and the C ABI of include/pi.h) for gfx950.
+
+Run as `python -m sparse_activation_ffn_amd.build`; hipcc cross-compiles, no
+GPU is needed.  The library is written next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpi.so")
+SOURCES = [os.path.join(CSRC, "pi_api.hip")]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("pi_device.h", "pi_kernels.h")] + \
+    [os.path.join(INCLUDE, "pi.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 instructions stay off: only plain fp32 VALU ops are emitted
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile libpi.so.  With force=False an up-to-date library is kept."""
+    if not force and os.path.exists(LIB):
+        newest = max(os.path.getmtime(p) for p in DEPS)
+        if os.path.getmtime(LIB) >= newest:
+            return LIB
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force=True, verbose="-v" in sys.argv))

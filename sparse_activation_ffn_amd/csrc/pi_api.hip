@@ -1,0 +1,510 @@
+// pi_api.hip -- host side of the C ABI declared in include/pi.h: argument
+// validation (before anything is enqueued), workspace layout, launch shapes,
+// template dispatch and the kernel timing hooks.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "pi.h"
+#include "pi_kernels.h"
+
+using namespace pi;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pi_status fail(pi_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+#define CHECK(cond, status, ...)                          \
+    do {                                                  \
+        if (!(cond)) return fail(status, __VA_ARGS__);    \
+    } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- workspace layout -------------------------------------------------------
+// [0, 8 KiB)   synchronisation counters (persist between calls, left at zero)
+//              word 0: predictor "last workgroup" counter
+//              words 64 .. 64+MAX_SLICES: down-kernel slice counters
+// [8 KiB, ...) per-call scratch: u [B][r] for the predictor; h [B][n] then
+//              chunk partials [nch][B][d] for the FFN.
+constexpr size_t WS_CTR_BYTES = 8192;
+constexpr int CTR_PRED = 0;
+constexpr int CTR_SLICE = 64;
+constexpr int MAX_SLICES = 1024;
+constexpr int NCH_MAX = 64;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int down_cols(int wt) { return wt == F32 ? Down<F32>::COLS : wt == F16 ? Down<F16>::COLS : Down<Q4>::COLS; }
+
+int pick_nch(int d, int wt, int B) {
+    const int slices = (d + down_cols(wt) - 1) / down_cols(wt);
+    int nch = 512 / slices;
+    if (B > 8) nch = nch * 8 / B;
+    return nch < 2 ? 2 : nch > NCH_MAX ? NCH_MAX : nch;
+}
+
+size_t ws_pred_bytes(int r, int B) { return WS_CTR_BYTES + align256((size_t)B * r * 4); }
+
+size_t ws_ffn_bytes(int d, int n, int B, int nch) {
+    return WS_CTR_BYTES + align256((size_t)B * n * 4) + align256((size_t)nch * B * d * 4);
+}
+
+// ---- timing hooks --------------------------------------------------------------
+struct Timer {
+    bool armed = false;
+    int max = 0, used = 0;
+    std::vector<hipEvent_t> ev;   // 2 per launch
+};
+thread_local Timer g_timers[PI_K_COUNT];
+
+template <typename K, typename... Args>
+pi_status launch(int kid, K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                 Args... args) {
+    Timer& t = g_timers[kid];
+    if (t.armed && t.used < t.max) {
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, t.ev[2 * t.used],
+                              t.ev[2 * t.used + 1], 0, args...);
+        ++t.used;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(PI_ERR_HIP, "%s launch: %s", pi_kernel_name(kid), hipGetErrorString(e));
+    return PI_OK;
+}
+
+int batch_tile(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+// ---- argument checks ----------------------------------------------------------------
+pi_status check_dtype_x(int xdtype) {
+    CHECK(xdtype == PI_F32 || xdtype == PI_F16, PI_ERR_DTYPE, "x dtype must be PI_F32 or PI_F16");
+    return PI_OK;
+}
+
+pi_status check_part(const pi_ffn_part* p, const char* name, bool allow_empty) {
+    CHECK(p, PI_ERR_ARG, "%s: NULL partition", name);
+    CHECK(p->wdtype == PI_F32 || p->wdtype == PI_F16 || p->wdtype == PI_Q4_0, PI_ERR_DTYPE,
+          "%s: wdtype must be PI_F32, PI_F16 or PI_Q4_0", name);
+    CHECK(p->act == PI_RELU || p->act == PI_REGLU, PI_ERR_ARG, "%s: act must be PI_RELU or PI_REGLU", name);
+    CHECK(p->d > 0 && p->d % 64 == 0, PI_ERR_SHAPE, "%s: d must be a positive multiple of 64", name);
+    CHECK(p->wdtype != PI_Q4_0 || p->d % 256 == 0, PI_ERR_SHAPE, "%s: Q4_0 rows need d %% 256 == 0", name);
+    CHECK(p->d <= down_cols(p->wdtype) * MAX_SLICES, PI_ERR_SHAPE, "%s: d too large", name);
+    CHECK(p->rows >= 0 && (allow_empty || p->rows > 0), PI_ERR_SHAPE, "%s: bad row count", name);
+    if (p->rows == 0) return PI_OK;
+    CHECK(p->W_up && p->W_downT, PI_ERR_ARG, "%s: W_up and W_downT are required", name);
+    CHECK(p->act == PI_RELU || p->W_gate, PI_ERR_ARG, "%s: ReGLU needs W_gate", name);
+    CHECK(aligned(p->W_up, 16) && aligned(p->W_downT, 16) &&
+              (p->act == PI_RELU || aligned(p->W_gate, 16)),
+          PI_ERR_ALIGN, "%s: weights must be 16-byte aligned", name);
+    CHECK(aligned(p->b_up, 4) && aligned(p->b_gate, 4), PI_ERR_ALIGN, "%s: biases must be 4-byte aligned", name);
+    return PI_OK;
+}
+
+pi_status check_ws(void* ws, size_t have, size_t need) {
+    CHECK(ws, PI_ERR_WORKSPACE, "workspace is NULL");
+    CHECK(aligned(ws, 256), PI_ERR_ALIGN, "workspace must be 256-byte aligned");
+    CHECK(have >= need, PI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return PI_OK;
+}
+
+#define TRY(expr)                         \
+    do {                                  \
+        pi_status _s = (expr);            \
+        if (_s != PI_OK) return _s;       \
+    } while (0)
+
+// ---- template dispatch ---------------------------------------------------------
+template <int WT, int XT, int BT>
+pi_status launch_pred_l1(const pi_predictor* p, const void* x, int B, float* u, hipStream_t s) {
+    return launch(PI_K_PRED_L1, k_pred_l1<WT, XT, BT>, dim3(p->r), dim3(THREADS), 0, s,
+                  (const uint8_t*)p->P1t, (const uint8_t*)x, p->d, p->r, B, u);
+}
+
+template <int WT, int XT>
+pi_status pred_l1_bt(const pi_predictor* p, const void* x, int B, float* u, hipStream_t s) {
+    switch (batch_tile(B)) {
+    case 1: return launch_pred_l1<WT, XT, 1>(p, x, B, u, s);
+    case 2: return launch_pred_l1<WT, XT, 2>(p, x, B, u, s);
+    case 4: return launch_pred_l1<WT, XT, 4>(p, x, B, u, s);
+    default: return launch_pred_l1<WT, XT, 8>(p, x, B, u, s);
+    }
+}
+
+template <int WT, int BT>
+pi_status launch_pred_l2(const pi_predictor* p, const float* u, int B, uint64_t* mask, float* logits,
+                         int fuse, Lists L, unsigned* ctr, hipStream_t s) {
+    const int grid = (p->n + 63) / 64;
+    return launch(PI_K_PRED_L2, k_pred_l2<WT, BT>, dim3(grid), dim3(THREADS),
+                  (size_t)BT * p->r * sizeof(float), s, (const uint8_t*)p->P2t, p->b2,
+                  p->threshold, u, p->n, p->r, B, mask, logits, fuse, L, ctr);
+}
+
+template <int WT>
+pi_status pred_l2_bt(const pi_predictor* p, const float* u, int B, uint64_t* mask, float* logits,
+                     int fuse, Lists L, unsigned* ctr, hipStream_t s) {
+    switch (batch_tile(B)) {
+    case 1: return launch_pred_l2<WT, 1>(p, u, B, mask, logits, fuse, L, ctr, s);
+    case 2: return launch_pred_l2<WT, 2>(p, u, B, mask, logits, fuse, L, ctr, s);
+    case 4: return launch_pred_l2<WT, 4>(p, u, B, mask, logits, fuse, L, ctr, s);
+    default: return launch_pred_l2<WT, 8>(p, u, B, mask, logits, fuse, L, ctr, s);
+    }
+}
+
+template <int WT, int XT, int BT, int ACT>
+pi_status launch_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
+    int grid = (rows_cap + NWAVES - 1) / NWAVES;
+    if (grid > 2048) grid = 2048;
+    if (grid < 1) grid = 1;
+    return launch(PI_K_UP, k_up<WT, XT, BT, ACT>, dim3(grid), dim3(THREADS), 0, s, a);
+}
+
+template <int WT, int BT>
+pi_status launch_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
+    const int slices = (a.d + Down<WT>::COLS - 1) / Down<WT>::COLS;
+    return launch(PI_K_DOWN, k_down<WT, BT>, dim3(slices, o.nch), dim3(THREADS), 0, s, a, o);
+}
+
+template <int WT, int XT, int BT>
+pi_status ffn_act(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
+    pi_status st = act == PI_RELU ? launch_up<WT, XT, BT, RELU>(a, rows_cap, s)
+                                  : launch_up<WT, XT, BT, REGLU>(a, rows_cap, s);
+    if (st != PI_OK) return st;
+    return launch_down<WT, BT>(a, o, s);
+}
+
+template <int WT, int XT>
+pi_status ffn_bt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
+    switch (batch_tile(a.B)) {
+    case 1: return ffn_act<WT, XT, 1>(a, o, act, rows_cap, s);
+    case 2: return ffn_act<WT, XT, 2>(a, o, act, rows_cap, s);
+    case 4: return ffn_act<WT, XT, 4>(a, o, act, rows_cap, s);
+    default: return ffn_act<WT, XT, 8>(a, o, act, rows_cap, s);
+    }
+}
+
+pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, int rows_cap,
+                  hipStream_t s) {
+    if (wt == F32) return xt == F32 ? ffn_bt<F32, F32>(a, o, act, rows_cap, s) : ffn_bt<F32, F16>(a, o, act, rows_cap, s);
+    if (wt == F16) return xt == F32 ? ffn_bt<F16, F32>(a, o, act, rows_cap, s) : ffn_bt<F16, F16>(a, o, act, rows_cap, s);
+    return xt == F32 ? ffn_bt<Q4, F32>(a, o, act, rows_cap, s) : ffn_bt<Q4, F16>(a, o, act, rows_cap, s);
+}
+
+// Shared body of pi_sparse_ffn / pi_sparse_ffn_split / pi_dense_ffn.
+pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x, int B,
+                     int xdtype, const int32_t* idx0, const int32_t* idx1, const int32_t* counts,
+                     bool dense, float* y0, float* y1, float* y, void* ws, size_t ws_bytes,
+                     hipStream_t s) {
+    TRY(check_part(hot, "hot", !dense));
+    const bool has_cold = cold && cold->rows > 0;
+    if (cold) TRY(check_part(cold, "cold", true));
+    if (has_cold) {
+        CHECK(cold->d == hot->d && cold->wdtype == hot->wdtype && cold->act == hot->act,
+              PI_ERR_SHAPE, "hot and cold partitions differ in d, wdtype or act");
+    }
+    TRY(check_dtype_x(xdtype));
+    CHECK(B >= 1 && B <= PI_MAX_BATCH, PI_ERR_SHAPE, "B must be in 1..%d", PI_MAX_BATCH);
+    CHECK(x && aligned(x, 16), x ? PI_ERR_ALIGN : PI_ERR_ARG, "x must be non-NULL and 16-byte aligned");
+    CHECK(y0 || y1 || y, PI_ERR_ARG, "no output given");
+    CHECK(aligned(y0, 16) && aligned(y1, 16) && aligned(y, 16), PI_ERR_ALIGN, "outputs must be 16-byte aligned");
+    if (!dense) {
+        CHECK(counts && aligned(counts, 4), counts ? PI_ERR_ALIGN : PI_ERR_ARG, "counts must be non-NULL, 4-byte aligned");
+        CHECK(hot->rows == 0 || (idx0 && aligned(idx0, 4)), PI_ERR_ARG, "hot index list missing");
+        CHECK(!has_cold || (idx1 && aligned(idx1, 4)), PI_ERR_ARG, "cold index list missing");
+    }
+    const int d = hot->d, wt = hot->wdtype;
+    const int n = hot->rows + (has_cold ? cold->rows : 0);
+    const int nch = pick_nch(d, wt, B);
+    TRY(check_ws(ws, ws_bytes, ws_ffn_bytes(d, n, B, nch)));
+
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    FfnArgs a{};
+    a.up[0] = (const uint8_t*)hot->W_up;
+    a.gate[0] = (const uint8_t*)hot->W_gate;
+    a.bup[0] = hot->b_up;
+    a.bgate[0] = hot->b_gate;
+    a.down[0] = (const uint8_t*)hot->W_downT;
+    a.idx[0] = dense ? nullptr : idx0;
+    if (has_cold) {
+        a.up[1] = (const uint8_t*)cold->W_up;
+        a.gate[1] = (const uint8_t*)cold->W_gate;
+        a.bup[1] = cold->b_up;
+        a.bgate[1] = cold->b_gate;
+        a.down[1] = (const uint8_t*)cold->W_downT;
+        a.idx[1] = idx1;
+    }
+    a.counts = dense ? nullptr : counts;
+    a.nparts = has_cold ? 2 : 1;
+    a.rows[0] = hot->rows;
+    a.rows[1] = has_cold ? cold->rows : 0;
+    a.dense_rows = dense ? hot->rows : 0;
+    a.d = d;
+    a.B = B;
+    a.rb = row_bytes(wt, d);
+    a.x = (const uint8_t*)x;
+    a.h = reinterpret_cast<float*>(base + WS_CTR_BYTES);
+    a.h_ld = n > 0 ? n : 1;
+    DownOut o{};
+    o.partials = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * n * 4));
+    o.ctr = reinterpret_cast<unsigned*>(base) + CTR_SLICE;
+    o.y_part[0] = y0;
+    o.y_part[1] = y1;
+    o.y = y;
+    o.nch = nch;
+    return run_ffn(a, o, wt, xdtype, hot->act, n, s);
+}
+
+}  // namespace
+
+// =================================================================================
+// C ABI
+// =================================================================================
+extern "C" {
+
+const char* pi_status_string(pi_status s) {
+    switch (s) {
+    case PI_OK: return "ok";
+    case PI_ERR_ARG: return "invalid argument";
+    case PI_ERR_SHAPE: return "invalid shape";
+    case PI_ERR_ALIGN: return "misaligned pointer";
+    case PI_ERR_DTYPE: return "unsupported dtype";
+    case PI_ERR_WORKSPACE: return "workspace too small";
+    case PI_ERR_BUDGET: return "invalid budget";
+    case PI_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* pi_last_error(void) { return g_err; }
+
+const char* pi_kernel_name(int32_t kid) {
+    static const char* names[PI_K_COUNT] = {"k_pred_l1", "k_pred_l2", "k_compact", "k_up", "k_down",
+                                            "k_merge", "k_profile", "k_index", "k_copy"};
+    return (kid >= 0 && kid < PI_K_COUNT) ? names[kid] : "?";
+}
+
+size_t pi_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t B) {
+    if (d <= 0 || n <= 0 || r <= 0 || B <= 0 || B > PI_MAX_BATCH) return 0;
+    size_t need = ws_pred_bytes(r, B);
+    for (int wt = F32; wt <= Q4; ++wt) {
+        size_t f = ws_ffn_bytes(d, n, B, pick_nch(d, wt, B));
+        if (f > need) need = f;
+    }
+    return need;
+}
+
+pi_status pi_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    CHECK(ws && aligned(ws, 256), PI_ERR_ALIGN, "workspace must be non-NULL and 256-byte aligned");
+    CHECK(ws_bytes >= WS_CTR_BYTES && ws_bytes % 16 == 0, PI_ERR_WORKSPACE, "workspace too small");
+    const int64_t n16 = (int64_t)(ws_bytes / 16);
+    int grid = (int)((n16 + THREADS - 1) / THREADS);
+    if (grid > 4096) grid = 4096;
+    return launch(PI_K_COPY, k_zero, dim3(grid), dim3(THREADS), 0, (hipStream_t)stream,
+                  reinterpret_cast<u4*>(ws), n16);
+}
+
+pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xdtype,
+                     uint64_t* mask, float* logits, const pi_active_lists* lists, void* ws,
+                     size_t ws_bytes, void* stream) {
+    CHECK(p, PI_ERR_ARG, "NULL predictor");
+    CHECK(p->wdtype == PI_F32 || p->wdtype == PI_F16, PI_ERR_DTYPE, "predictor wdtype must be PI_F32 or PI_F16");
+    TRY(check_dtype_x(xdtype));
+    CHECK(p->d > 0 && p->d % 64 == 0, PI_ERR_SHAPE, "d must be a positive multiple of 64");
+    CHECK(p->r > 0 && p->r % 16 == 0 && p->r <= 4096, PI_ERR_SHAPE, "r must be a multiple of 16 in 16..4096");
+    CHECK(p->n > 0 && p->n <= (1 << 24), PI_ERR_SHAPE, "n must be in 1..2^24");
+    CHECK(B >= 1 && B <= PI_MAX_BATCH, PI_ERR_SHAPE, "B must be in 1..%d", PI_MAX_BATCH);
+    CHECK(p->P1t && p->P2t && x && mask, PI_ERR_ARG, "P1t, P2t, x and mask are required");
+    CHECK(aligned(p->P1t, 16) && aligned(p->P2t, 16) && aligned(x, 16), PI_ERR_ALIGN,
+          "P1t, P2t and x must be 16-byte aligned");
+    CHECK(aligned(mask, 8) && aligned(logits, 4) && aligned(p->b2, 4), PI_ERR_ALIGN, "mask/logits/b2 misaligned");
+    Lists L{};
+    if (lists) {
+        CHECK(lists->n_hot >= 0 && lists->n_hot <= p->n, PI_ERR_SHAPE, "lists->n_hot out of range");
+        CHECK(lists->counts && aligned(lists->counts, 8), PI_ERR_ARG, "lists->counts required (8-byte aligned)");
+        CHECK(lists->n_hot == 0 || lists->hot_idx, PI_ERR_ARG, "lists->hot_idx required");
+        CHECK(lists->n_hot == p->n || lists->cold_idx, PI_ERR_ARG, "lists->cold_idx required");
+        L = Lists{lists->n_hot, lists->hot_idx, lists->cold_idx, lists->counts};
+    }
+    TRY(check_ws(ws, ws_bytes, ws_pred_bytes(p->r, B)));
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    float* u = reinterpret_cast<float*>(base + WS_CTR_BYTES);
+    unsigned* ctr = reinterpret_cast<unsigned*>(base) + CTR_PRED;
+    hipStream_t s = (hipStream_t)stream;
+    const int wt = p->wdtype;
+    pi_status st;
+    if (wt == F32)
+        st = xdtype == F32 ? pred_l1_bt<F32, F32>(p, x, B, u, s) : pred_l1_bt<F32, F16>(p, x, B, u, s);
+    else
+        st = xdtype == F32 ? pred_l1_bt<F16, F32>(p, x, B, u, s) : pred_l1_bt<F16, F16>(p, x, B, u, s);
+    TRY(st);
+    const int fuse = lists ? 1 : 0;
+    return wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, fuse, L, ctr, s)
+                     : pred_l2_bt<F16>(p, u, B, mask, logits, fuse, L, ctr, s);
+}
+
+pi_status pi_compact_active(const uint64_t* mask, int32_t n, const pi_active_lists* lists,
+                            void* stream) {
+    CHECK(mask && aligned(mask, 8), PI_ERR_ARG, "mask required (8-byte aligned)");
+    CHECK(n > 0 && n <= (1 << 24), PI_ERR_SHAPE, "n must be in 1..2^24");
+    CHECK(lists, PI_ERR_ARG, "lists required");
+    CHECK(lists->n_hot >= 0 && lists->n_hot <= n, PI_ERR_SHAPE, "lists->n_hot out of range");
+    CHECK(lists->counts && aligned(lists->counts, 8), PI_ERR_ARG, "lists->counts required (8-byte aligned)");
+    CHECK(lists->n_hot == 0 || lists->hot_idx, PI_ERR_ARG, "lists->hot_idx required");
+    CHECK(lists->n_hot == n || lists->cold_idx, PI_ERR_ARG, "lists->cold_idx required");
+    Lists L{lists->n_hot, lists->hot_idx, lists->cold_idx, lists->counts};
+    return launch(PI_K_COMPACT, k_compact, dim3(1), dim3(THREADS), 0, (hipStream_t)stream, mask, n, L);
+}
+
+pi_status pi_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                        const int32_t* idx, const int32_t* count, float* y, void* ws,
+                        size_t ws_bytes, void* stream) {
+    CHECK(y, PI_ERR_ARG, "y required");
+    CHECK(count && aligned(count, 4), PI_ERR_ARG, "count required (4-byte aligned)");
+    // a single partition runs as the hot half of a split with no cold part:
+    // items are idx[0 .. *count) and only count[0] is read
+    return ffn_common(part, nullptr, x, B, xdtype, idx, nullptr, count, false, nullptr, nullptr,
+                      y, ws, ws_bytes, (hipStream_t)stream);
+}
+
+pi_status pi_sparse_ffn_split(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                              int32_t B, int32_t xdtype, const pi_active_lists* lists,
+                              float* y_hot, float* y_cold, float* y, void* ws, size_t ws_bytes,
+                              void* stream) {
+    CHECK(lists, PI_ERR_ARG, "lists required");
+    CHECK(hot && lists->n_hot == hot->rows, PI_ERR_SHAPE, "lists->n_hot must equal hot->rows");
+    return ffn_common(hot, cold, x, B, xdtype, lists->hot_idx, lists->cold_idx, lists->counts,
+                      false, y_hot, y_cold, y, ws, ws_bytes, (hipStream_t)stream);
+}
+
+pi_status pi_dense_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype, float* y,
+                       void* ws, size_t ws_bytes, void* stream) {
+    CHECK(y, PI_ERR_ARG, "y required");
+    return ffn_common(part, nullptr, x, B, xdtype, nullptr, nullptr, nullptr, true, nullptr,
+                      nullptr, y, ws, ws_bytes, (hipStream_t)stream);
+}
+
+pi_status pi_merge(const float* y_hot, const float* y_cold, int32_t B, int32_t d, float* y,
+                   void* stream) {
+    CHECK(y_hot && y, PI_ERR_ARG, "y_hot and y are required");
+    CHECK(B >= 1 && d >= 1, PI_ERR_SHAPE, "B and d must be positive");
+    CHECK(aligned(y_hot, 4) && aligned(y_cold, 4) && aligned(y, 4), PI_ERR_ALIGN, "misaligned output");
+    const int64_t len = (int64_t)B * d;
+    int grid = (int)((len + THREADS - 1) / THREADS);
+    if (grid > 1024) grid = 1024;
+    return launch(PI_K_MERGE, k_merge, dim3(grid), dim3(THREADS), 0, (hipStream_t)stream, y_hot,
+                  y_cold, len, y);
+}
+
+pi_status pi_profile_counts(const pi_ffn_part* part, const void* X, int32_t S, int32_t xdtype,
+                            uint32_t* counts, void* stream) {
+    TRY(check_part(part, "part", false));
+    TRY(check_dtype_x(xdtype));
+    CHECK(S >= 0, PI_ERR_SHAPE, "S must be >= 0");
+    CHECK(counts && aligned(counts, 4), PI_ERR_ARG, "counts required");
+    CHECK(S == 0 || (X && aligned(X, 16)), PI_ERR_ARG, "X required (16-byte aligned)");
+    const bool reglu = part->act == PI_REGLU;
+    const uint8_t* W = (const uint8_t*)(reglu ? part->W_gate : part->W_up);
+    const float* bias = reglu ? part->b_gate : part->b_up;
+    const int grid = (part->rows + NWAVES - 1) / NWAVES;
+    hipStream_t s = (hipStream_t)stream;
+    const int wt = part->wdtype;
+#define PROF(WT_, XT_) launch(PI_K_PROFILE, k_profile<WT_, XT_, 8>, dim3(grid), dim3(THREADS), 0, s, \
+                              W, bias, (const uint8_t*)X, part->d, part->rows, S, counts)
+    if (wt == F32) return xdtype == F32 ? PROF(F32, F32) : PROF(F32, F16);
+    if (wt == F16) return xdtype == F32 ? PROF(F16, F32) : PROF(F16, F16);
+    return xdtype == F32 ? PROF(Q4, F32) : PROF(Q4, F16);
+#undef PROF
+}
+
+pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budget_bytes,
+                                int64_t bytes_per_neuron, int32_t* perm, int32_t* n_hot,
+                                void* stream) {
+    CHECK(n >= 0 && n <= (1 << 24), PI_ERR_SHAPE, "n must be in 0..2^24");
+    CHECK(budget_bytes >= 0 && bytes_per_neuron > 0, PI_ERR_BUDGET,
+          "budget must be >= 0 and bytes_per_neuron > 0");
+    CHECK(n_hot, PI_ERR_ARG, "n_hot required");
+    CHECK(n == 0 || (counts && perm && aligned(counts, 4) && aligned(perm, 4)), PI_ERR_ARG,
+          "counts and perm required");
+    const int64_t k = budget_bytes / bytes_per_neuron;
+    *n_hot = (int32_t)(k < n ? k : n);
+    if (n == 0) return PI_OK;
+    return launch(PI_K_INDEX, k_index, dim3((n + THREADS - 1) / THREADS), dim3(THREADS), 0,
+                  (hipStream_t)stream, counts, n, perm);
+}
+
+pi_status pi_permute_rows(const void* src, void* dst, const int32_t* perm, int32_t rows,
+                          int64_t row_bytes_, void* stream) {
+    CHECK(rows >= 0 && row_bytes_ > 0 && row_bytes_ % 4 == 0, PI_ERR_SHAPE,
+          "rows >= 0 and row_bytes a positive multiple of 4");
+    if (rows == 0) return PI_OK;
+    CHECK(src && dst && perm, PI_ERR_ARG, "src, dst and perm required");
+    CHECK(aligned(src, 4) && aligned(dst, 4) && aligned(perm, 4), PI_ERR_ALIGN, "misaligned");
+    const uint8_t* s0 = (const uint8_t*)src;
+    const uint8_t* d0 = (const uint8_t*)dst;
+    const int64_t total = (int64_t)rows * row_bytes_;
+    CHECK(d0 + total <= s0 || s0 + total <= d0, PI_ERR_ARG, "src and dst overlap");
+    return launch(PI_K_COPY, k_permute_rows, dim3(rows), dim3(THREADS), 0, (hipStream_t)stream,
+                  (const uint32_t*)src, (uint32_t*)dst, perm, row_bytes_ / 4);
+}
+
+pi_status pi_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    CHECK(bytes >= 0 && bytes % 16 == 0, PI_ERR_SHAPE, "bytes must be a multiple of 16");
+    if (bytes == 0) return PI_OK;
+    CHECK(src && dst && aligned(src, 16) && aligned(dst, 16), PI_ERR_ALIGN, "src/dst 16-byte aligned");
+    const int64_t n16 = bytes / 16;
+    int64_t grid = (n16 + THREADS - 1) / THREADS;
+    if (grid > 8192) grid = 8192;
+    return launch(PI_K_COPY, k_copy, dim3((unsigned)grid), dim3(THREADS), 0, (hipStream_t)stream,
+                  (const u4*)src, (u4*)dst, n16);
+}
+
+pi_status pi_kernel_timer_start(int32_t kid, int32_t max_launches) {
+    CHECK(kid >= 0 && kid < PI_K_COUNT, PI_ERR_ARG, "bad kernel id");
+    CHECK(max_launches >= 1 && max_launches <= 100000, PI_ERR_ARG, "max_launches in 1..100000");
+    Timer& t = g_timers[kid];
+    while ((int)t.ev.size() < 2 * max_launches) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return fail(PI_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+        t.ev.push_back(e);
+    }
+    t.armed = true;
+    t.max = max_launches;
+    t.used = 0;
+    return PI_OK;
+}
+
+pi_status pi_kernel_timer_stop(int32_t kid, float* total_ms, int32_t* launches) {
+    CHECK(kid >= 0 && kid < PI_K_COUNT, PI_ERR_ARG, "bad kernel id");
+    CHECK(total_ms && launches, PI_ERR_ARG, "outputs required");
+    Timer& t = g_timers[kid];
+    float sum = 0.0f;
+    for (int i = 0; i < t.used; ++i) {
+        hipError_t err = hipEventSynchronize(t.ev[2 * i + 1]);
+        if (err != hipSuccess) return fail(PI_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(err));
+        float ms = 0.0f;
+        err = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+        if (err != hipSuccess) return fail(PI_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(err));
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = t.used;
+    t.armed = false;
+    t.used = 0;
+    return PI_OK;
+}
+
+}  // extern "C"

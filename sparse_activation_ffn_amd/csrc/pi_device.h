@@ -1,0 +1,248 @@
+// pi_device.h -- device helpers of the sparse-FFN kernels for gfx950 (CDNA4, wave64).
+//
+// A weight row is read in 16-byte "chunks" with one 16-byte load per lane, so a
+// wave moves 1 KiB per load instruction and every 128-byte line it touches is
+// used whole.  Elements per chunk: f32 4, f16 8, Q4_0 32 (16 code bytes plus
+// the block's fp16 scale, which sits in the row's scale plane).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pi {
+
+constexpr int WAVE = 64;
+enum { F32 = 0, F16 = 1, Q4 = 2 };
+enum { RELU = 0, REGLU = 1 };
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+}
+__device__ __forceinline__ u4 ld16(const void* p) { return *reinterpret_cast<const u4*>(p); }
+__device__ __forceinline__ u2 ld8_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+}
+__device__ __forceinline__ float bits_f(unsigned v) { return __builtin_bit_cast(float, v); }
+__device__ __forceinline__ h2 bits_h2(unsigned v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ float half_lo(unsigned v) { return (float)bits_h2(v).x; }
+__device__ __forceinline__ float half_hi(unsigned v) { return (float)bits_h2(v).y; }
+__device__ __forceinline__ float half_f(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
+
+// Row bytes of one neuron's row of d elements.
+__host__ __device__ __forceinline__ int64_t row_bytes(int wt, int64_t d) {
+    return wt == F32 ? 4 * d : wt == F16 ? 2 * d : d / 2 + d / 16;
+}
+
+// ---- dot products of one weight chunk with the matching x elements ---------
+//
+// x is read from `xp`, which points at the chunk's first x element of one
+// token (global or LDS memory), stored as float (XT == F32) or half (XT == F16).
+
+template <int WT> struct Chunk;
+template <> struct Chunk<F32> { static constexpr int EPC = 4; };
+template <> struct Chunk<F16> { static constexpr int EPC = 8; };
+template <> struct Chunk<Q4> { static constexpr int EPC = 32; };
+
+template <int WT, int XT> struct Dot;
+
+template <> struct Dot<F32, F32> {
+    __device__ static float run(u4 w, float, const void* xp, float acc) {
+        f4 x = *reinterpret_cast<const f4*>(xp);
+        acc = fmaf(bits_f(w.x), x.x, acc);
+        acc = fmaf(bits_f(w.y), x.y, acc);
+        acc = fmaf(bits_f(w.z), x.z, acc);
+        acc = fmaf(bits_f(w.w), x.w, acc);
+        return acc;
+    }
+};
+
+template <> struct Dot<F32, F16> {
+    __device__ static float run(u4 w, float, const void* xp, float acc) {
+        u2 x = *reinterpret_cast<const u2*>(xp);
+        acc = fmaf(bits_f(w.x), half_lo(x.x), acc);
+        acc = fmaf(bits_f(w.y), half_hi(x.x), acc);
+        acc = fmaf(bits_f(w.z), half_lo(x.y), acc);
+        acc = fmaf(bits_f(w.w), half_hi(x.y), acc);
+        return acc;
+    }
+};
+
+template <> struct Dot<F16, F16> {
+    // half x half products are exact in fp32; v_dot2 adds two of them per op
+    __device__ static float run(u4 w, float, const void* xp, float acc) {
+        u4 x = *reinterpret_cast<const u4*>(xp);
+        acc = __builtin_amdgcn_fdot2(bits_h2(w.x), bits_h2(x.x), acc, false);
+        acc = __builtin_amdgcn_fdot2(bits_h2(w.y), bits_h2(x.y), acc, false);
+        acc = __builtin_amdgcn_fdot2(bits_h2(w.z), bits_h2(x.z), acc, false);
+        acc = __builtin_amdgcn_fdot2(bits_h2(w.w), bits_h2(x.w), acc, false);
+        return acc;
+    }
+};
+
+template <> struct Dot<F16, F32> {
+    __device__ static float run(u4 w, float, const void* xp, float acc) {
+        const f4* x = reinterpret_cast<const f4*>(xp);
+        f4 a = x[0], b = x[1];
+        acc = fmaf(half_lo(w.x), a.x, acc);
+        acc = fmaf(half_hi(w.x), a.y, acc);
+        acc = fmaf(half_lo(w.y), a.z, acc);
+        acc = fmaf(half_hi(w.y), a.w, acc);
+        acc = fmaf(half_lo(w.z), b.x, acc);
+        acc = fmaf(half_hi(w.z), b.y, acc);
+        acc = fmaf(half_lo(w.w), b.z, acc);
+        acc = fmaf(half_hi(w.w), b.w, acc);
+        return acc;
+    }
+};
+
+// Q4_0 block: code byte t holds element t (low nibble) and t + 16 (high nibble).
+// Two codes go into one half2 as 1024 + q (exponent 10, so the integer is exact),
+// and subtracting 1032 leaves q - 8 exactly; v_dot2 then takes two products.
+__device__ __forceinline__ h2 q4_pair(unsigned two_bytes_in_halves) {
+    h2 v = bits_h2((two_bytes_in_halves & 0x000F000Fu) | 0x64006400u);
+    return v - h2{(_Float16)1032.0f, (_Float16)1032.0f};
+}
+
+template <> struct Dot<Q4, F16> {
+    // w: 16 code bytes of one block; s: the block's scale; xp: 32 halves
+    __device__ static float run(u4 w, float s, const void* xp, float acc) {
+        const u4* xv = reinterpret_cast<const u4*>(xp);
+        u4 xl0 = xv[0], xl1 = xv[1], xh0 = xv[2], xh1 = xv[3];
+        unsigned cw[4] = {w.x, w.y, w.z, w.w};
+        unsigned xl[8] = {xl0.x, xl0.y, xl0.z, xl0.w, xl1.x, xl1.y, xl1.z, xl1.w};
+        unsigned xh[8] = {xh0.x, xh0.y, xh0.z, xh0.w, xh1.x, xh1.y, xh1.z, xh1.w};
+        float blk = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // bytes (0,1) and (2,3) of code dword m moved into the two halves
+            unsigned b01 = __builtin_amdgcn_perm(cw[m], cw[m], 0x0C010C00u);
+            unsigned b23 = __builtin_amdgcn_perm(cw[m], cw[m], 0x0C030C02u);
+            blk = __builtin_amdgcn_fdot2(q4_pair(b01), bits_h2(xl[2 * m]), blk, false);
+            blk = __builtin_amdgcn_fdot2(q4_pair(b23), bits_h2(xl[2 * m + 1]), blk, false);
+            blk = __builtin_amdgcn_fdot2(q4_pair(b01 >> 4), bits_h2(xh[2 * m]), blk, false);
+            blk = __builtin_amdgcn_fdot2(q4_pair(b23 >> 4), bits_h2(xh[2 * m + 1]), blk, false);
+        }
+        return fmaf(blk, s, acc);
+    }
+};
+
+template <> struct Dot<Q4, F32> {
+    __device__ static float run(u4 w, float s, const void* xp, float acc) {
+        const float* x = reinterpret_cast<const float*>(xp);
+        unsigned cw[4] = {w.x, w.y, w.z, w.w};
+        float blk = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            unsigned byte = (cw[t >> 2] >> (8 * (t & 3))) & 0xffu;
+            blk = fmaf((float)(int)(byte & 15u) - 8.0f, x[t], blk);
+            blk = fmaf((float)(int)(byte >> 4) - 8.0f, x[t + 16], blk);
+        }
+        return fmaf(blk, s, acc);
+    }
+};
+
+// ---- axpy of one weight chunk into per-lane accumulators (down projection) --
+//
+// The down kernel gives each lane DCH consecutive columns of a row:
+// f32 4 (16 B), f16 8 (16 B), Q4_0 16 (8 code bytes = half a block: elements
+// k0..k0+7 and k0+16..k0+23 of the block, k0 = 0 or 8, plus the block scale).
+
+template <int WT> struct Down;
+
+template <> struct Down<F32> {
+    static constexpr int DCH = 4;     // columns per lane
+    static constexpr int COLS = 256;  // columns per wave-wide slice
+    typedef u4 raw;
+    __device__ static raw load(const uint8_t* row, int64_t d, int col0) {
+        return ld16_stream(row + 4 * (int64_t)col0);
+    }
+    __device__ static void axpy(raw w, float h, float* acc) {
+        acc[0] = fmaf(h, bits_f(w.x), acc[0]);
+        acc[1] = fmaf(h, bits_f(w.y), acc[1]);
+        acc[2] = fmaf(h, bits_f(w.z), acc[2]);
+        acc[3] = fmaf(h, bits_f(w.w), acc[3]);
+    }
+    // column of accumulator e, relative to the lane's first column
+    __device__ static int col(int e) { return e; }
+};
+
+template <> struct Down<F16> {
+    static constexpr int DCH = 8;
+    static constexpr int COLS = 512;
+    typedef u4 raw;
+    __device__ static raw load(const uint8_t* row, int64_t d, int col0) {
+        return ld16_stream(row + 2 * (int64_t)col0);
+    }
+    __device__ static void axpy(raw w, float h, float* acc) {
+        acc[0] = fmaf(h, half_lo(w.x), acc[0]);
+        acc[1] = fmaf(h, half_hi(w.x), acc[1]);
+        acc[2] = fmaf(h, half_lo(w.y), acc[2]);
+        acc[3] = fmaf(h, half_hi(w.y), acc[3]);
+        acc[4] = fmaf(h, half_lo(w.z), acc[4]);
+        acc[5] = fmaf(h, half_hi(w.z), acc[5]);
+        acc[6] = fmaf(h, half_lo(w.w), acc[6]);
+        acc[7] = fmaf(h, half_hi(w.w), acc[7]);
+    }
+    __device__ static int col(int e) { return e; }
+};
+
+struct Q4Half { u2 codes; float scale; };
+
+template <> struct Down<Q4> {
+    static constexpr int DCH = 16;
+    static constexpr int COLS = 1024;   // 32 blocks, two lanes per block
+    typedef Q4Half raw;
+    // col0 = first column of this lane's half block: 32*j + k0 with k0 in {0, 8}
+    __device__ static raw load(const uint8_t* row, int64_t d, int col0) {
+        int j = col0 >> 5, k0 = col0 & 31;
+        Q4Half r;
+        r.codes = ld8_stream(row + 16 * (int64_t)j + k0);
+        r.scale = half_f(*reinterpret_cast<const uint16_t*>(row + d / 2 + 2 * (int64_t)j));
+        return r;
+    }
+    __device__ static void axpy(raw w, float h, float* acc) {
+        float hs = h * w.scale;
+        unsigned cw[2] = {w.codes.x, w.codes.y};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            unsigned byte = (cw[t >> 2] >> (8 * (t & 3))) & 0xffu;
+            acc[t] = fmaf(hs, (float)(int)(byte & 15u) - 8.0f, acc[t]);
+            acc[8 + t] = fmaf(hs, (float)(int)(byte >> 4) - 8.0f, acc[8 + t]);
+        }
+    }
+    // accumulators 0..7 -> columns k0..k0+7, 8..15 -> columns k0+16..k0+23
+    __device__ static int col(int e) { return e < 8 ? e : e + 8; }
+};
+
+// ---- reductions ------------------------------------------------------------
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    // sum over aligned groups of W lanes (W a power of two <= 64)
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<WAVE>(v); }
+
+// Device-scope (all XCDs) synchronisation helpers for "last workgroup done"
+// reductions: every thread fences its stores, one thread counts arrivals.
+__device__ __forceinline__ unsigned arrive(unsigned* ctr) {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(unsigned* ctr) {
+    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace pi

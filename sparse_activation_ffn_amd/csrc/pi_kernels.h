@@ -1,0 +1,566 @@
+// pi_kernels.h -- HIP kernels of the predictor-gated sparse FFN (gfx950).
+//
+// One decode layer step runs four kernels on one stream, with the active
+// counts kept in device memory so the host never waits inside a step:
+//   k_pred_l1   u = ReLU(P1t x)                       (dense rows of P1t)
+//   k_pred_l2   logit = P2t u + b2, > threshold, OR over tokens -> mask words;
+//               its last workgroup compacts the mask into hot/cold lists
+//   k_up        gathered rows of W_up (and W_gate) -> h per active neuron
+//   k_down      gathered rows of W_downT scaled by h, 2-D tiled over
+//               (column slice x neuron chunk); the last chunk of each slice
+//               reduces the chunk partials in a fixed order into y_hot,
+//               y_cold and y = y_hot + y_cold (the merge)
+// Method: PowerInfer pages -- CSDN article, sections on sparse activation
+// (predict, then compute only predicted neurons) and on the hybrid design
+// (per-partition computation of the predicted neurons, then a merge).
+#pragma once
+#include "pi_device.h"
+
+namespace pi {
+
+constexpr int THREADS = 256;          // 4 waves per workgroup for every kernel here
+constexpr int NWAVES = THREADS / WAVE;
+
+// ===========================================================================
+// Predictor, first layer: u[b][j] = max(0, P1t[j] . x_b).  One workgroup per
+// row j; threads stride over the row's 16-byte chunks; token groups of BT.
+// ===========================================================================
+template <int WT, int XT, int BT>
+__global__ __launch_bounds__(THREADS) void k_pred_l1(const uint8_t* __restrict__ P1t,
+                                                     const uint8_t* __restrict__ x, int d, int r,
+                                                     int B, float* __restrict__ u) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int XB = XT == F32 ? 4 : 2;
+    __shared__ float red[NWAVES][BT];
+    const int j = blockIdx.x;
+    const int nch = d / EPC;
+    const uint8_t* row = P1t + (int64_t)j * row_bytes(WT, d);
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    for (int b0 = 0; b0 < B; b0 += BT) {
+        float acc[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
+        for (int c = threadIdx.x; c < nch; c += THREADS) {
+            u4 w = ld16_stream(row + 16 * (int64_t)c);
+#pragma unroll
+            for (int b = 0; b < BT; ++b)
+                if (b0 + b < B)
+                    acc[b] = Dot<WT, XT>::run(w, 0.0f, x + ((int64_t)(b0 + b) * d + c * EPC) * XB,
+                                              acc[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            float v = wave_sum(acc[b]);
+            if (lane == 0) red[wv][b] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x < BT && b0 + (int)threadIdx.x < B) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) s += red[w][threadIdx.x];
+            u[(int64_t)(b0 + threadIdx.x) * r + j] = s > 0.0f ? s : 0.0f;
+        }
+        __syncthreads();
+    }
+}
+
+// ===========================================================================
+// Compaction of mask words into ascending hot / cold lists, by one workgroup.
+// Thread t owns a contiguous run of words, so an exclusive scan of per-thread
+// popcounts gives each set bit its position in the ascending list.
+// ===========================================================================
+struct Lists {
+    int32_t n_hot;
+    int32_t* hot;
+    int32_t* cold;
+    int32_t* counts;
+};
+
+__device__ void compact_block(const uint64_t* mask, int n, Lists L, bool coherent) {
+    __shared__ int s_tot[THREADS];
+    __shared__ int s_hot[THREADS];
+    const int words = (n + 63) / 64;
+    const int per = (words + THREADS - 1) / THREADS;
+    const int w0 = threadIdx.x * per, w1 = min(words, w0 + per);
+    // bits at or beyond n are ignored, so lists never exceed their capacities
+    const uint64_t tail = (n % 64) ? ((1ull << (n % 64)) - 1ull) : ~0ull;
+    int tot = 0, hot = 0;
+    for (int w = w0; w < w1; ++w) {
+        uint64_t v = coherent ? load_coherent(mask + w) : mask[w];
+        if (w == words - 1) v &= tail;
+        tot += __popcll(v);
+        int lo = 64 * w;
+        if (lo + 64 <= L.n_hot) hot += __popcll(v);
+        else if (lo < L.n_hot) hot += __popcll(v & ((1ull << (L.n_hot - lo)) - 1ull));
+    }
+    s_tot[threadIdx.x] = tot;
+    s_hot[threadIdx.x] = hot;
+    __syncthreads();
+    // inclusive scan of totals (Hillis-Steele) and a sum of hot counts
+    for (int o = 1; o < THREADS; o <<= 1) {
+        int a = threadIdx.x >= o ? s_tot[threadIdx.x - o] : 0;
+        int h = threadIdx.x >= o ? s_hot[threadIdx.x - o] : 0;
+        __syncthreads();
+        s_tot[threadIdx.x] += a;
+        s_hot[threadIdx.x] += h;
+        __syncthreads();
+    }
+    const int H = s_hot[THREADS - 1];
+    const int T = s_tot[THREADS - 1];
+    int pos = s_tot[threadIdx.x] - tot;
+    for (int w = w0; w < w1; ++w) {
+        uint64_t v = coherent ? load_coherent(mask + w) : mask[w];
+        if (w == words - 1) v &= tail;
+        while (v) {
+            int bit = __builtin_ctzll(v);
+            v &= v - 1;
+            int id = 64 * w + bit;
+            if (id < L.n_hot) L.hot[pos] = id;
+            else L.cold[pos - H] = id - L.n_hot;
+            ++pos;
+        }
+    }
+    if (threadIdx.x == 0) {
+        L.counts[0] = H;
+        L.counts[1] = T - H;
+    }
+}
+
+__global__ __launch_bounds__(THREADS) void k_compact(const uint64_t* __restrict__ mask, int n,
+                                                     Lists L) {
+    compact_block(mask, n, L, false);
+}
+
+// ===========================================================================
+// Predictor, second layer + threshold + union over tokens, one mask word (64
+// neurons) per workgroup.  Each wave owns 16 rows of P2t; 16 lanes share a row
+// (4 rows per load instruction, 256 contiguous bytes per row).  u is staged in
+// LDS per token group.  With `fuse`, the last workgroup to finish compacts the
+// whole mask into the active lists.
+// ===========================================================================
+template <int WT, int BT>
+__global__ __launch_bounds__(THREADS) void k_pred_l2(const uint8_t* __restrict__ P2t,
+                                                     const float* __restrict__ b2, float thr,
+                                                     const float* __restrict__ u, int n, int r,
+                                                     int B, uint64_t* __restrict__ mask,
+                                                     float* __restrict__ logits, int fuse, Lists L,
+                                                     unsigned* ctr) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int G = 16;                       // lanes per row
+    extern __shared__ float s_u[];              // [BT][r]
+    __shared__ unsigned s_flag[64];
+    __shared__ int s_last;
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int gi = lane / G, li = lane % G;
+    const int nch = r / EPC;
+    const int64_t rb = row_bytes(WT, r);
+    if (threadIdx.x < 64) s_flag[threadIdx.x] = 0;
+    for (int b0 = 0; b0 < B; b0 += BT) {
+        const int nb = min(BT, B - b0);
+        __syncthreads();
+        for (int k = threadIdx.x; k < nb * r; k += THREADS) s_u[k] = u[(int64_t)b0 * r + k];
+        for (int k = nb * r + threadIdx.x; k < BT * r; k += THREADS) s_u[k] = 0.0f;
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int loc = 16 * wv + 4 * p + gi;        // neuron within the word
+            const int i = 64 * blockIdx.x + loc;
+            float acc[BT];
+#pragma unroll
+            for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
+            if (i < n) {
+                const uint8_t* row = P2t + (int64_t)i * rb;
+                for (int c = li; c < nch; c += G) {
+                    u4 w = ld16_stream(row + 16 * (int64_t)c);
+#pragma unroll
+                    for (int b = 0; b < BT; ++b)
+                        acc[b] = Dot<WT, F32>::run(w, 0.0f, s_u + b * r + c * EPC, acc[b]);
+                }
+            }
+            unsigned fire = 0;
+            const float bias = (i < n && b2) ? b2[i] : 0.0f;
+#pragma unroll
+            for (int b = 0; b < BT; ++b) {
+                float lg = group_sum<G>(acc[b]) + bias;
+                if (b < nb) {
+                    fire |= lg > thr;
+                    if (logits && li == 0 && i < n) logits[(int64_t)(b0 + b) * n + i] = lg;
+                }
+            }
+            if (li == 0 && i < n) s_flag[loc] |= fire;
+        }
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const int i = 64 * blockIdx.x + lane;
+        uint64_t word = __ballot(i < n && s_flag[lane] != 0);
+        if (lane == 0) mask[blockIdx.x] = word;
+    }
+    if (!fuse) return;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = arrive(ctr) == gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    compact_block(mask, n, L, true);
+    if (threadIdx.x == 0) reset_counter(ctr);
+}
+
+// ===========================================================================
+// Gathered rows of the FFN.  Work items are the active neurons of both
+// partitions: items [0, H) are hot_idx[0..H), items [H, H+C) cold_idx[0..C).
+// In dense mode (no lists) item k is row k of partition 0.
+// ===========================================================================
+struct FfnArgs {
+    const uint8_t* up[2];
+    const uint8_t* gate[2];
+    const float* bup[2];
+    const float* bgate[2];
+    const uint8_t* down[2];
+    const int32_t* idx[2];
+    const int32_t* counts;   // device [nparts] active counts (NULL in dense mode)
+    int nparts;              // 1 (no cold partition) or 2
+    int rows[2];             // rows of each partition (list capacity and id bound)
+    int dense_rows;          // dense mode: rows of partition 0
+    int d;
+    int B;
+    int64_t rb;              // row bytes
+    const uint8_t* x;        // [B][d]
+    float* h;                // [B][h_ld] per item
+    int h_ld;
+};
+
+__device__ __forceinline__ void item_counts(const FfnArgs& a, int& H, int& C) {
+    if (a.counts) {
+        // counts beyond the lists' capacities are clamped (never read past a list)
+        H = min(max(a.counts[0], 0), a.rows[0]);
+        C = a.nparts > 1 ? min(max(a.counts[1], 0), a.rows[1]) : 0;
+    } else {
+        H = a.dense_rows;
+        C = 0;
+    }
+}
+
+__device__ __forceinline__ void item_row(const FfnArgs& a, int item, int H, int& part, int& row) {
+    if (item < H) {
+        part = 0;
+        row = a.idx[0] ? a.idx[0][item] : item;
+    } else {
+        part = 1;
+        row = a.idx[1][item - H];
+    }
+}
+
+// Up/gate: one wave per item; lanes stride over the row's chunks, U chunks in
+// flight per lane; the wave reduces; lane 0 applies bias and activation.
+template <int WT, int XT, int BT, int ACT>
+__global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int XB = XT == F32 ? 4 : 2;
+    constexpr int U = WT == Q4 ? 4 : 8;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int gw = (blockIdx.x * THREADS + threadIdx.x) / WAVE;
+    const int nw = gridDim.x * NWAVES;
+    int H, C;
+    item_counts(a, H, C);
+    const int T = H + C;
+    const int nch = a.d / EPC;
+    for (int item = gw; item < T; item += nw) {
+        int part, row;
+        item_row(a, item, H, part, row);
+        if ((unsigned)row >= (unsigned)a.rows[part]) {     // id outside the partition: h = 0
+            if (lane == 0)
+                for (int b = 0; b < a.B; ++b) a.h[(int64_t)b * a.h_ld + item] = 0.0f;
+            continue;
+        }
+        const uint8_t* wu = a.up[part] + (int64_t)row * a.rb;
+        const uint8_t* wg = ACT == REGLU ? a.gate[part] + (int64_t)row * a.rb : nullptr;
+        for (int b0 = 0; b0 < a.B; b0 += BT) {
+            float au[BT], ag[BT];
+#pragma unroll
+            for (int b = 0; b < BT; ++b) au[b] = ag[b] = 0.0f;
+            for (int c0 = lane; c0 < nch; c0 += WAVE * U) {
+                u4 vu[U], vg[U];
+                float su[U], sg[U];
+#pragma unroll
+                for (int k = 0; k < U; ++k) {
+                    const int c = c0 + WAVE * k;
+                    if (c < nch) {
+                        vu[k] = ld16_stream(wu + 16 * (int64_t)c);
+                        su[k] = WT == Q4 ? half_f(*(const uint16_t*)(wu + a.d / 2 + 2 * c)) : 0.f;
+                        if (ACT == REGLU) {
+                            vg[k] = ld16_stream(wg + 16 * (int64_t)c);
+                            sg[k] = WT == Q4 ? half_f(*(const uint16_t*)(wg + a.d / 2 + 2 * c))
+                                             : 0.f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < U; ++k) {
+                    const int c = c0 + WAVE * k;
+                    if (c < nch) {
+#pragma unroll
+                        for (int b = 0; b < BT; ++b) {
+                            if (b0 + b < a.B) {
+                                const uint8_t* xp = a.x + ((int64_t)(b0 + b) * a.d + c * EPC) * XB;
+                                au[b] = Dot<WT, XT>::run(vu[k], su[k], xp, au[b]);
+                                if (ACT == REGLU) ag[b] = Dot<WT, XT>::run(vg[k], sg[k], xp, ag[b]);
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < BT; ++b) {
+                float up = wave_sum(au[b]);
+                float g = ACT == REGLU ? wave_sum(ag[b]) : 0.0f;
+                if (lane == 0 && b0 + b < a.B) {
+                    up += a.bup[part] ? a.bup[part][row] : 0.0f;
+                    float hv;
+                    if (ACT == RELU) {
+                        hv = up > 0.0f ? up : 0.0f;
+                    } else {
+                        g += a.bgate[part] ? a.bgate[part][row] : 0.0f;
+                        hv = (g > 0.0f ? g : 0.0f) * up;
+                    }
+                    a.h[(int64_t)(b0 + b) * a.h_ld + item] = hv;
+                }
+            }
+        }
+    }
+}
+
+// Down: grid (column slices, neuron chunks).  Chunks are split between the
+// partitions in proportion to their active counts so no chunk mixes them.
+// Each wave walks the chunk's items with stride NWAVES, U rows in flight; the
+// four waves reduce through LDS; the chunk writes its partial; the last chunk
+// of the slice sums the partials in chunk order into y_hot / y_cold / y.
+struct DownOut {
+    float* partials;    // [nch][B][d]
+    unsigned* ctr;      // [slices]
+    float* y_part[2];   // [B][d] or NULL
+    float* y;           // [B][d] or NULL
+    int nch;
+};
+
+__device__ __forceinline__ void chunk_range(int nch, int H, int C, int k, int& part, int& lo,
+                                            int& hi, int& nh) {
+    const int T = H + C;
+    if (C == 0) nh = nch;
+    else if (H == 0) nh = 0;
+    else nh = min(nch - 1, max(1, (int)(((int64_t)nch * H + T / 2) / T)));
+    if (k < nh) {
+        part = 0;
+        lo = (int)((int64_t)k * H / nh);
+        hi = (int)((int64_t)(k + 1) * H / nh);
+    } else {
+        const int kk = k - nh, nc = nch - nh;
+        part = 1;
+        lo = (int)((int64_t)kk * C / nc);
+        hi = (int)((int64_t)(kk + 1) * C / nc);
+    }
+}
+
+template <int WT, int BT>
+__global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
+    using D = Down<WT>;
+    constexpr int DCH = D::DCH;
+    constexpr int U = 8;
+    __shared__ float s_red[NWAVES - 1][DCH][WAVE];
+    __shared__ int s_last;
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int slice = blockIdx.x, k = blockIdx.y;
+    // this lane's first column: lanes cover D::COLS consecutive columns
+    const int lane_col = WT == Q4 ? 32 * (lane >> 1) + 8 * (lane & 1) : lane * DCH;
+    const int col0 = slice * D::COLS + lane_col;
+    const bool active_col = col0 < a.d;
+    int H, C;
+    item_counts(a, H, C);
+    int part, lo, hi, nh;
+    chunk_range(o.nch, H, C, k, part, lo, hi, nh);
+    const int hbase = part == 0 ? 0 : H;
+    const int B = a.B;
+    for (int b0 = 0; b0 < B; b0 += BT) {
+        float acc[BT][DCH];
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+            for (int e = 0; e < DCH; ++e) acc[b][e] = 0.0f;
+        for (int it0 = lo + wv; it0 < hi; it0 += NWAVES * U) {
+            typename D::raw w[U];
+            float hv[U][BT];
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int it = it0 + NWAVES * q;
+                if (it < hi) {
+                    int row = a.idx[part] ? a.idx[part][it] : it;
+                    if ((unsigned)row >= (unsigned)a.rows[part]) row = 0;   // its h is 0
+                    if (active_col) w[q] = D::load(a.down[part] + (int64_t)row * a.rb, a.d, col0);
+#pragma unroll
+                    for (int b = 0; b < BT; ++b)
+                        hv[q][b] = b0 + b < B ? a.h[(int64_t)(b0 + b) * a.h_ld + hbase + it] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int it = it0 + NWAVES * q;
+                if (it < hi && active_col) {
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) D::axpy(w[q], hv[q][b], acc[b]);
+                }
+            }
+        }
+        // reduce the four waves' accumulators, one token at a time through LDS
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            if (b0 + b < B) {                       // uniform across the workgroup
+                if (wv > 0) {
+#pragma unroll
+                    for (int e = 0; e < DCH; ++e) s_red[wv - 1][e][lane] = acc[b][e];
+                }
+                __syncthreads();
+                if (wv == 0 && active_col) {
+                    float* prow = o.partials + ((int64_t)k * B + b0 + b) * a.d + col0;
+#pragma unroll
+                    for (int e = 0; e < DCH; ++e) {
+                        float s = acc[b][e];
+#pragma unroll
+                        for (int w = 1; w < NWAVES; ++w) s += s_red[w - 1][e][lane];
+                        prow[D::col(e)] = s;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+    // the last chunk of this slice reduces the partials in chunk order
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = arrive(o.ctr + slice) == (unsigned)o.nch - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int c0 = slice * D::COLS;
+    const int ncols = min(D::COLS, a.d - c0);
+    for (int t = threadIdx.x; t < ncols * B; t += THREADS) {
+        const int b = t / ncols, c = c0 + t % ncols;
+        float yh = 0.0f, yc = 0.0f;
+        for (int kk = 0; kk < nh; ++kk)
+            yh += load_coherent(o.partials + ((int64_t)kk * B + b) * a.d + c);
+        for (int kk = nh; kk < o.nch; ++kk)
+            yc += load_coherent(o.partials + ((int64_t)kk * B + b) * a.d + c);
+        const int64_t at = (int64_t)b * a.d + c;
+        if (o.y_part[0]) o.y_part[0][at] = yh;
+        if (o.y_part[1]) o.y_part[1][at] = yc;
+        if (o.y) o.y[at] = yh + yc;
+    }
+    if (threadIdx.x == 0) reset_counter(o.ctr + slice);
+}
+
+// ===========================================================================
+// Merge of two partial outputs: y = a + b (b may be NULL).
+// ===========================================================================
+__global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ a,
+                                                   const float* __restrict__ b, int64_t len,
+                                                   float* __restrict__ y) {
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < len; i += stride)
+        y[i] = b ? a[i] + b[i] : a[i];
+}
+
+// ===========================================================================
+// Offline profiling: counts[i] = #{s : pre_i(X_s) > 0}.  One wave per row,
+// samples in groups of BT.  (Offline, not on the decode path.)
+// ===========================================================================
+template <int WT, int XT, int BT>
+__global__ __launch_bounds__(THREADS) void k_profile(const uint8_t* __restrict__ W,
+                                                     const float* __restrict__ bias,
+                                                     const uint8_t* __restrict__ X, int d, int rows,
+                                                     int S, uint32_t* __restrict__ counts) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int XB = XT == F32 ? 4 : 2;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int row = (blockIdx.x * THREADS + threadIdx.x) / WAVE;
+    if (row >= rows) return;
+    const int64_t rb = row_bytes(WT, d);
+    const uint8_t* w = W + (int64_t)row * rb;
+    const int nch = d / EPC;
+    const float bi = bias ? bias[row] : 0.0f;
+    uint32_t cnt = 0;
+    for (int s0 = 0; s0 < S; s0 += BT) {
+        float acc[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
+        for (int c = lane; c < nch; c += WAVE) {
+            u4 v = ld16(w + 16 * (int64_t)c);
+            float sc = WT == Q4 ? half_f(*(const uint16_t*)(w + d / 2 + 2 * c)) : 0.0f;
+#pragma unroll
+            for (int b = 0; b < BT; ++b)
+                if (s0 + b < S)
+                    acc[b] = Dot<WT, XT>::run(v, sc, X + ((int64_t)(s0 + b) * d + c * EPC) * XB,
+                                              acc[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            float pre = wave_sum(acc[b]) + bi;
+            cnt += (s0 + b < S && pre > 0.0f) ? 1u : 0u;
+        }
+    }
+    if (lane == 0) counts[row] = cnt;
+}
+
+// ===========================================================================
+// Neuron index: rank_i = #{j : c_j > c_i} + #{j < i : c_j == c_i}; perm[rank_i] = i.
+// Exact, deterministic, O(n^2) compares over LDS tiles of the counts.
+// ===========================================================================
+__global__ __launch_bounds__(THREADS) void k_index(const uint32_t* __restrict__ counts, int n,
+                                                   int32_t* __restrict__ perm) {
+    constexpr int TILE = 4096;
+    __shared__ uint32_t s_c[TILE];
+    const int i = blockIdx.x * THREADS + threadIdx.x;
+    const uint32_t ci = i < n ? counts[i] : 0u;
+    int rank = 0;
+    for (int t0 = 0; t0 < n; t0 += TILE) {
+        const int len = min(TILE, n - t0);
+        __syncthreads();
+        for (int k = threadIdx.x; k < len; k += THREADS) s_c[k] = counts[t0 + k];
+        __syncthreads();
+        if (i < n) {
+            for (int k = 0; k < len; ++k) {
+                const uint32_t cj = s_c[k];
+                rank += (cj > ci) | ((cj == ci) & (t0 + k < i));
+            }
+        }
+    }
+    if (i < n) perm[rank] = i;
+}
+
+// dst row s = src row perm[s]; 4-byte words.
+__global__ __launch_bounds__(THREADS) void k_permute_rows(const uint32_t* __restrict__ src,
+                                                          uint32_t* __restrict__ dst,
+                                                          const int32_t* __restrict__ perm,
+                                                          int64_t words_per_row) {
+    const int s = blockIdx.x;
+    const int p = perm[s];
+    if ((unsigned)p >= gridDim.x) return;      // not a row id: dst row left as it was
+    const uint32_t* from = src + (int64_t)p * words_per_row;
+    uint32_t* to = dst + (int64_t)s * words_per_row;
+    for (int64_t k = threadIdx.x; k < words_per_row; k += THREADS) to[k] = from[k];
+}
+
+// Plain 16-byte copy (traffic calibration); also used to zero workspaces.
+__global__ __launch_bounds__(THREADS) void k_copy(const u4* __restrict__ src, u4* __restrict__ dst,
+                                                  int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(THREADS) void k_zero(u4* __restrict__ dst, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n16; i += stride)
+        dst[i] = u4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace pi

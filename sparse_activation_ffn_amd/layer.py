@@ -1,0 +1,125 @@
+"""One FFN layer with its predictor resident in device memory, driven through
+the C ABI: offline profiling -> neuron index -> row permutation, and the
+decode step predict(+compact) -> sparse FFN over hot and cold -> merge.
+
+PowerInfer pages: CSDN article, overall-architecture section (offline
+profiling and placement, online per-partition computation and merge) and
+hybrid-design figure.  Only torch allocations and C calls happen here.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as pb
+
+
+def _dev(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceLayer:
+    """Device tensors of one layer.  Per-neuron tensors are row-major [n][...]."""
+
+    def __init__(self, d, n, r, act, wdtype_q4, W_up, W_gate, W_downT, b_up, b_gate, P1t, P2t,
+                 b2, threshold=0.0, n_hot=None):
+        self.d, self.n, self.r = d, n, r
+        self.act = pb.PI_REGLU if act in ("reglu", pb.PI_REGLU) else pb.PI_RELU
+        self.q4 = wdtype_q4
+        self.W_up, self.W_gate, self.W_downT = W_up, W_gate, W_downT
+        self.b_up, self.b_gate = b_up, b_gate
+        self.P1t, self.P2t, self.b2 = P1t, P2t, b2
+        self.threshold = float(threshold)
+        self.n_hot = n if n_hot is None else n_hot
+        self.row_bytes = W_up.shape[1] * W_up.element_size()
+
+    @classmethod
+    def upload(cls, L, device="cuda", n_hot=None):
+        """From a workload.synth.Layer (numpy) to device memory."""
+        return cls(L.d, L.n, L.r, L.wl.act, L.wl.wdtype == "q4_0", _dev(L.W_up, device),
+                   _dev(L.W_gate, device), _dev(L.W_downT, device), _dev(L.b_up, device),
+                   _dev(L.b_gate, device), _dev(L.P1t, device), _dev(L.P2t, device),
+                   _dev(L.b2, device), L.threshold, n_hot)
+
+    def clone(self):
+        """Same values at new device addresses (another instance of the layer)."""
+        c = lambda t: None if t is None else t.clone()  # noqa: E731
+        return DeviceLayer(self.d, self.n, self.r, self.act, self.q4, c(self.W_up), c(self.W_gate),
+                           c(self.W_downT), c(self.b_up), c(self.b_gate), c(self.P1t),
+                           c(self.P2t), c(self.b2), self.threshold, self.n_hot)
+
+    # ---- descriptors ---------------------------------------------------------
+    def predictor(self) -> pb.Predictor:
+        return pb.make_predictor(self.P1t, self.P2t, self.b2, self.threshold)
+
+    def part(self, lo=0, hi=None) -> pb.FfnPart:
+        hi = self.n if hi is None else hi
+        s = lambda t: pb.row_slice(t, lo, hi)  # noqa: E731
+        return pb.make_part(self.d, s(self.W_up), s(self.W_downT), self.act, s(self.W_gate),
+                            s(self.b_up), s(self.b_gate), q4=self.q4)
+
+    def parts(self):
+        hot = self.part(0, self.n_hot)
+        cold = self.part(self.n_hot, self.n) if self.n_hot < self.n else None
+        return hot, cold
+
+    # ---- offline: profiling and neuron index ----------------------------------
+    def profile_counts(self, X: torch.Tensor) -> torch.Tensor:
+        counts = torch.empty(self.n, dtype=torch.int32, device=X.device)
+        pb.pi_profile_counts(self.part(), X, counts)
+        return counts
+
+    def build_index(self, counts: torch.Tensor, budget_bytes: int, bytes_per_neuron: int):
+        perm = torch.empty(self.n, dtype=torch.int32, device=counts.device)
+        n_hot = pb.pi_build_neuron_index(counts, budget_bytes, bytes_per_neuron, perm)
+        return perm, n_hot
+
+    def apply_index(self, perm: torch.Tensor, n_hot: int):
+        """Permute every per-neuron tensor by perm (slot -> original id)."""
+        def permute(t):
+            if t is None:
+                return None
+            out = torch.empty_like(t)
+            rb = t[0].numel() * t.element_size() if t.dim() > 1 else t.element_size()
+            pb.pi_permute_rows(t, out, perm, self.n, rb)
+            return out
+        self.W_up, self.W_gate, self.W_downT = (permute(self.W_up), permute(self.W_gate),
+                                                permute(self.W_downT))
+        self.b_up, self.b_gate = permute(self.b_up), permute(self.b_gate)
+        self.P2t, self.b2 = permute(self.P2t), permute(self.b2)
+        self.n_hot = n_hot
+
+
+class StepBuffers:
+    """Mask, active lists, outputs and workspace for decode steps of one shape."""
+
+    def __init__(self, layer: DeviceLayer, B: int, device="cuda"):
+        n, d = layer.n, layer.d
+        self.B = B
+        self.mask = torch.zeros((n + 63) // 64, dtype=torch.int64, device=device)
+        self.hot_idx = torch.zeros(max(layer.n_hot, 1), dtype=torch.int32, device=device)
+        self.cold_idx = torch.zeros(max(n - layer.n_hot, 1), dtype=torch.int32, device=device)
+        self.counts = torch.zeros(2, dtype=torch.int32, device=device)
+        self.y = torch.zeros((B, d), dtype=torch.float32, device=device)
+        self.y_hot = torch.zeros((B, d), dtype=torch.float32, device=device)
+        self.y_cold = torch.zeros((B, d), dtype=torch.float32, device=device)
+        wsb = pb.pi_workspace_bytes(d, n, layer.r, B)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+        pb.pi_workspace_init(self.ws)
+        self.lists = pb.make_lists(layer.n_hot, self.hot_idx,
+                                   self.cold_idx if layer.n_hot < n else None, self.counts)
+
+
+def decode_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, pred=None, parts=None,
+                partials: bool = False, stream=None):
+    """predict (+fused compaction) -> sparse FFN on hot and cold -> merge, on one stream."""
+    pred = layer.predictor() if pred is None else pred
+    hot, cold = layer.parts() if parts is None else parts
+    pb.pi_predict(pred, x, buf.mask, None, buf.lists, buf.ws, stream)
+    pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, buf.y_hot if partials else None,
+                           buf.y_cold if partials else None, buf.y, buf.ws, stream)
+    return buf.y

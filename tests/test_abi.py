@@ -1,0 +1,140 @@
+"""C ABI checks that need no GPU: libpi.so loads, exports every entry point
+include/pi.h declares, and rejects bad arguments before enqueueing anything
+(only calls that fail validation are made here, so no kernel is launched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_activation_ffn_amd import binding as pb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pi_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return pb.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(pb.EXPORTS)
+
+
+def test_status_strings(L):
+    assert L.pi_status_string(0) == b"ok"
+    assert L.pi_status_string(pb.PI_ERR_WORKSPACE) == b"workspace too small"
+    assert L.pi_kernel_name(pb.PI_K_DOWN) == b"k_down"
+
+
+def test_workspace_bytes(L):
+    assert L.pi_workspace_bytes(0, 10, 16, 1) == 0
+    assert L.pi_workspace_bytes(64, 10, 16, pb.PI_MAX_BATCH + 1) == 0
+    a = L.pi_workspace_bytes(7168, 28672, 1024, 1)
+    b = L.pi_workspace_bytes(7168, 28672, 1024, 4)
+    assert 8192 < a < b
+    # h [B][n] and partials fit: at least 8 KiB + n*4 + d*4*2
+    assert a >= 8192 + 28672 * 4 + 7168 * 4 * 2
+
+
+FAKE = 0x10000      # never dereferenced: every call below fails validation first
+
+
+def _pred(**kw):
+    p = dict(d=64, n=100, r=16, wdtype=pb.PI_F16, P1t=FAKE, P2t=FAKE, b2=None, threshold=0.0)
+    p.update(kw)
+    return pb.Predictor(**p)
+
+
+def _call_predict(L, pred, x=FAKE, B=1, xdt=pb.PI_F16, mask=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.pi_predict(C.byref(pred) if pred is not None else None, x, B, xdt, mask, None, None,
+                        ws, wsb, None)
+
+
+def test_predict_validation(L):
+    assert _call_predict(L, None) == pb.PI_ERR_ARG
+    assert _call_predict(L, _pred(wdtype=pb.PI_Q4_0)) == pb.PI_ERR_DTYPE
+    assert _call_predict(L, _pred(), xdt=7) == pb.PI_ERR_DTYPE
+    assert _call_predict(L, _pred(d=65)) == pb.PI_ERR_SHAPE
+    assert _call_predict(L, _pred(r=20)) == pb.PI_ERR_SHAPE
+    assert _call_predict(L, _pred(n=0)) == pb.PI_ERR_SHAPE
+    assert _call_predict(L, _pred(), B=0) == pb.PI_ERR_SHAPE
+    assert _call_predict(L, _pred(), B=pb.PI_MAX_BATCH + 1) == pb.PI_ERR_SHAPE
+    assert _call_predict(L, _pred(P1t=FAKE + 8)) == pb.PI_ERR_ALIGN
+    assert _call_predict(L, _pred(), mask=None) == pb.PI_ERR_ARG
+    assert _call_predict(L, _pred(), ws=None) == pb.PI_ERR_WORKSPACE
+    assert _call_predict(L, _pred(), wsb=100) == pb.PI_ERR_WORKSPACE
+    assert b"workspace" in L.pi_last_error()
+
+
+def _part(**kw):
+    p = dict(d=256, rows=100, wdtype=pb.PI_F16, act=pb.PI_RELU, W_up=FAKE, W_gate=None,
+             b_up=None, b_gate=None, W_downT=FAKE)
+    p.update(kw)
+    return pb.FfnPart(**p)
+
+
+def _call_sparse(L, part, B=1, xdt=pb.PI_F16, idx=FAKE, count=FAKE, y=FAKE, wsb=1 << 24):
+    return L.pi_sparse_ffn(C.byref(part), FAKE, B, xdt, idx, count, y, FAKE, wsb, None)
+
+
+def test_sparse_ffn_validation(L):
+    assert _call_sparse(L, _part(act=5)) == pb.PI_ERR_ARG
+    assert _call_sparse(L, _part(wdtype=9)) == pb.PI_ERR_DTYPE
+    assert _call_sparse(L, _part(d=100)) == pb.PI_ERR_SHAPE
+    assert _call_sparse(L, _part(d=320, wdtype=pb.PI_Q4_0)) == pb.PI_ERR_SHAPE
+    assert _call_sparse(L, _part(act=pb.PI_REGLU)) == pb.PI_ERR_ARG        # no W_gate
+    assert _call_sparse(L, _part(W_downT=FAKE + 4)) == pb.PI_ERR_ALIGN
+    assert _call_sparse(L, _part(), count=None) == pb.PI_ERR_ARG
+    assert _call_sparse(L, _part(), y=None) == pb.PI_ERR_ARG
+    assert _call_sparse(L, _part(), B=0) == pb.PI_ERR_SHAPE
+    assert _call_sparse(L, _part(), wsb=16) == pb.PI_ERR_WORKSPACE
+
+
+def test_split_validation(L):
+    hot, cold = _part(rows=30), _part(rows=70, d=512)
+    lists = pb.ActiveLists(30, FAKE, FAKE, FAKE)
+    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, C.byref(lists),
+                               None, None, FAKE, FAKE, 1 << 24, None)
+    assert rc == pb.PI_ERR_SHAPE          # hot and cold differ in d
+    lists.n_hot = 31
+    cold = _part(rows=70)
+    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, C.byref(lists),
+                               None, None, FAKE, FAKE, 1 << 24, None)
+    assert rc == pb.PI_ERR_SHAPE          # n_hot != hot rows
+
+
+def test_compact_merge_copy_validation(L):
+    lists = pb.ActiveLists(10, FAKE, None, FAKE)
+    assert L.pi_compact_active(FAKE, 20, C.byref(lists), None) == pb.PI_ERR_ARG   # cold missing
+    assert L.pi_compact_active(FAKE, 0, C.byref(lists), None) == pb.PI_ERR_SHAPE
+    assert L.pi_compact_active(FAKE + 4, 20, C.byref(lists), None) == pb.PI_ERR_ARG
+    assert L.pi_merge(None, None, 1, 8, FAKE, None) == pb.PI_ERR_ARG
+    assert L.pi_merge(FAKE, None, 0, 8, FAKE, None) == pb.PI_ERR_SHAPE
+    assert L.pi_copy(FAKE, FAKE, 15, None) == pb.PI_ERR_SHAPE
+    assert L.pi_permute_rows(FAKE, FAKE, FAKE, 4, 16, None) == pb.PI_ERR_ARG      # overlap
+    assert L.pi_permute_rows(FAKE, FAKE + 1024, FAKE, 4, 6, None) == pb.PI_ERR_SHAPE
+
+
+def test_neuron_index_host_side(L):
+    n_hot = C.c_int32(-1)
+    assert L.pi_build_neuron_index(FAKE, 10, -1, 4, FAKE, C.byref(n_hot), None) == pb.PI_ERR_BUDGET
+    assert L.pi_build_neuron_index(FAKE, 10, 40, 0, FAKE, C.byref(n_hot), None) == pb.PI_ERR_BUDGET
+    # n == 0 computes n_hot on the host and launches nothing
+    assert L.pi_build_neuron_index(None, 0, 1000, 7, None, C.byref(n_hot), None) == pb.PI_OK
+    assert n_hot.value == 0
+
+
+def test_timer_validation(L):
+    assert L.pi_kernel_timer_start(-1, 4) == pb.PI_ERR_ARG
+    assert L.pi_kernel_timer_start(pb.PI_K_UP, 0) == pb.PI_ERR_ARG
