@@ -40,13 +40,23 @@ __global__ __launch_bounds__(THREADS) void k_pred_l1(const uint8_t* __restrict__
         float acc[BT];
 #pragma unroll
         for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
-        for (int c = threadIdx.x; c < nch; c += THREADS) {
-            u4 w = ld16_stream(row + 16 * (int64_t)c);
+        constexpr int U = 4;                    // chunks in flight per thread
+        for (int c0 = threadIdx.x; c0 < nch; c0 += THREADS * U) {
+            u4 w[U];
 #pragma unroll
-            for (int b = 0; b < BT; ++b)
-                if (b0 + b < B)
-                    acc[b] = Dot<WT, XT>::run(w, 0.0f, x + ((int64_t)(b0 + b) * d + c * EPC) * XB,
-                                              acc[b]);
+            for (int q = 0; q < U; ++q)
+                if (c0 + THREADS * q < nch) w[q] = ld16_stream(row + 16 * (int64_t)(c0 + THREADS * q));
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int c = c0 + THREADS * q;
+                if (c < nch) {
+#pragma unroll
+                    for (int b = 0; b < BT; ++b)
+                        if (b0 + b < B)
+                            acc[b] = Dot<WT, XT>::run(
+                                w[q], 0.0f, x + ((int64_t)(b0 + b) * d + c * EPC) * XB, acc[b]);
+                }
+            }
         }
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
@@ -170,11 +180,22 @@ __global__ __launch_bounds__(THREADS) void k_pred_l2(const uint8_t* __restrict__
             for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
             if (i < n) {
                 const uint8_t* row = P2t + (int64_t)i * rb;
-                for (int c = li; c < nch; c += G) {
-                    u4 w = ld16_stream(row + 16 * (int64_t)c);
+                constexpr int U = 8;            // chunks in flight per lane (a 2 KiB row at once)
+                for (int c0 = li; c0 < nch; c0 += G * U) {
+                    u4 w[U];
 #pragma unroll
-                    for (int b = 0; b < BT; ++b)
-                        acc[b] = Dot<WT, F32>::run(w, 0.0f, s_u + b * r + c * EPC, acc[b]);
+                    for (int q = 0; q < U; ++q)
+                        if (c0 + G * q < nch) w[q] = ld16_stream(row + 16 * (int64_t)(c0 + G * q));
+#pragma unroll
+                    for (int q = 0; q < U; ++q) {
+                        const int c = c0 + G * q;
+                        if (c < nch) {
+#pragma unroll
+                            for (int b = 0; b < BT; ++b)
+                                acc[b] = Dot<WT, F32>::run(w[q], 0.0f, s_u + b * r + c * EPC,
+                                                           acc[b]);
+                        }
+                    }
                 }
             }
             unsigned fire = 0;
