@@ -1,9 +1,10 @@
 """Benchmark of the predictor-gated sparse FFN decode step on one MI355X.
 
 One step = one pass of the whole hot path over one token batch: predictor
-(both layers, threshold, union) with the compaction fused into its last
-workgroup, then the sparse FFN over the hot and the cold partition with the
-merge fused into the down projection's reduction.
+(both layers, threshold, union) and compaction into hot/cold lists
+(`pi_predict` with lists), then the sparse FFN over the hot and the cold
+partition with the merge fused into the reduction of the down projection's
+partials (`pi_sparse_ffn_split`).  Six kernels, no host synchronisation.
 
 Default workload: the OPT-30B-shaped ReLU layer (d_model 7168, d_ffn 28672,
 predictor rank 1024, fp16 weights, fp32 accumulation, batch 1), hot partition
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = ("sparse-FFN µs/layer + achieved HBM GB/s on touched weights vs peak, batch 1")
 PEAK_HBM_GBPS = 8000.0
 INSTANCES = 8
+COPY_CAL_BYTES = 512 << 20     # reads 512 MiB, writes 512 MiB
 
 
 def log(*a):
@@ -48,16 +50,20 @@ def wrow_bytes(wl):
     return wl.d // 2 + wl.d // 16 if wl.wdtype == "q4_0" else wl.d * esize(wl.wdtype)
 
 
-def kernel_bytes(wl, B, active, nch):
-    """Algorithmic bytes per launch of each kernel for one step with `active` neurons."""
+def kernel_bytes(wl, B, active):
+    """Algorithmic bytes per launch of each kernel for one step with `active` neurons:
+    the weights and inputs the step must read and the results it must write."""
     ep = esize(wl.pdtype)
     ex = esize(wl.xdtype)
     m_up = 2 if wl.act == "reglu" else 1
+    words = (wl.n + 63) // 64
     return {
         "k_pred_l1": wl.r * wl.d * ep + B * wl.d * ex + B * wl.r * 4,
-        "k_pred_l2": wl.n * wl.r * ep + 4 * wl.n + B * wl.r * 4 + wl.n // 8 + 4 * active,
+        "k_pred_l2": wl.n * wl.r * ep + 4 * wl.n + B * wl.r * 4 + 8 * words,
+        "k_compact": 8 * words + 4 * active + 8,
         "k_up": active * (m_up * wrow_bytes(wl) + 4 + 4) + B * wl.d * ex + 4 * B * active,
-        "k_down": active * (wrow_bytes(wl) + 4) + 4 * B * active + 4 * B * wl.d,
+        "k_down": active * (wrow_bytes(wl) + 4) + 4 * B * active,
+        "k_reduce": 4 * B * wl.d,
     }
 
 
@@ -155,8 +161,9 @@ def main():
 
     # second pass over the same steps: per-kernel durations from dispatch events, and the
     # active count of each step (deterministic, so identical to the first pass)
-    kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2, "k_up": pb.PI_K_UP,
-            "k_down": pb.PI_K_DOWN}
+    kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2,
+            "k_compact": pb.PI_K_COMPACT, "k_up": pb.PI_K_UP, "k_down": pb.PI_K_DOWN,
+            "k_reduce": pb.PI_K_REDUCE}
     for kid in kids.values():
         pb.pi_kernel_timer_start(kid, K)
     active = []
@@ -169,8 +176,7 @@ def main():
     kern_ms = {name: pb.pi_kernel_timer_stop(kid) for name, kid in kids.items()}
     kern_us = {name: ms * 1e3 / max(k, 1) for name, (ms, k) in kern_ms.items()}
     mean_active = float(np.mean(active))
-    nch_est = None
-    kb = [kernel_bytes(wl, B, a, nch_est) for a in active]
+    kb = [kernel_bytes(wl, B, a) for a in active]
     kb_mean = {k: float(np.mean([b[k] for b in kb])) for k in kb[0]}
     touched = float(np.mean([step_bytes(wl, B, a) for a in active]))
     gbps_touched = touched / (us_step * 1e-6) / 1e9
@@ -228,6 +234,15 @@ def main():
         "roofline": roofline, "dense_ffn": dense, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+    # a plain copy of known size, whose hardware byte counters calibrate the
+    # counter-based traffic figures taken from the same run
+    nbytes = COPY_CAL_BYTES
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        pb.pi_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

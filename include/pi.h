@@ -127,9 +127,8 @@ typedef struct pi_active_lists {
 size_t pi_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t B);
 
 /*
- * Zero-fills a workspace (with a fill kernel).  A workspace must be zeroed
- * once before its first use; every call leaves its synchronisation counters
- * at zero again, so it need not be re-zeroed between calls.
+ * Zero-fills a workspace (with a fill kernel).  Optional: calls keep no
+ * state in the workspace between them and need no particular contents.
  */
 pi_status pi_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
@@ -140,8 +139,7 @@ pi_status pi_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *          neuron i is active for some token; bits >= n are 0.
  *   logits [B][n] float32, out, or NULL.
  *   lists  optional: if not NULL, the same call also compacts the mask into
- *          ascending hot/cold lists (as pi_compact_active does), fused into
- *          the predictor's last workgroup.
+ *          ascending hot/cold lists (it enqueues pi_compact_active's kernel).
  * Needs a workspace (pi_workspace_bytes).
  */
 pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xdtype,
@@ -232,15 +230,16 @@ pi_status pi_copy(const void* src, void* dst, int64_t bytes, void* stream);
 /* Kernel ids for the timing hooks below. */
 enum {
     PI_K_PRED_L1 = 0,     /* predictor first layer */
-    PI_K_PRED_L2 = 1,     /* predictor second layer + threshold + union (+ compaction) */
-    PI_K_COMPACT = 2,     /* standalone compaction */
+    PI_K_PRED_L2 = 1,     /* predictor second layer + threshold + union */
+    PI_K_COMPACT = 2,     /* mask -> active lists */
     PI_K_UP = 3,          /* gathered-row up/gate + activation */
-    PI_K_DOWN = 4,        /* column-scatter down + reduction + merge */
+    PI_K_DOWN = 4,        /* column-scatter down into chunk partials */
     PI_K_MERGE = 5,       /* standalone merge */
     PI_K_PROFILE = 6,
     PI_K_INDEX = 7,
     PI_K_COPY = 8,
-    PI_K_COUNT = 9
+    PI_K_REDUCE = 9,      /* chunk partials -> y_hot, y_cold, y (fused merge) */
+    PI_K_COUNT = 10
 };
 
 /*

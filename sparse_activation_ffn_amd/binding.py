@@ -21,7 +21,7 @@ PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
 PI_RELU, PI_REGLU = 0, 1
 PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
- PI_K_INDEX, PI_K_COPY, PI_K_COUNT) = range(10)
+ PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_COUNT) = range(11)
 
 # every symbol include/pi.h declares
 EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_active",

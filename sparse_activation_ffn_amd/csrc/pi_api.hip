@@ -34,14 +34,11 @@ pi_status fail(pi_status s, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---- workspace layout -------------------------------------------------------
-// [0, 8 KiB)   synchronisation counters (persist between calls, left at zero)
-//              word 0: predictor "last workgroup" counter
-//              words 64 .. 64+MAX_SLICES: down-kernel slice counters
-// [8 KiB, ...) per-call scratch: u [B][r] for the predictor; h [B][n] then
-//              chunk partials [nch][B][d] for the FFN.
-constexpr size_t WS_CTR_BYTES = 8192;
-constexpr int CTR_PRED = 0;
-constexpr int CTR_SLICE = 64;
+// [0, 256)     reserved header
+// [256, ...)   per-call scratch: u [B][r] for the predictor; h [B][n] then
+//              chunk partials [nch][B][d] for the FFN.  Nothing persists
+//              between calls.
+constexpr size_t WS_CTR_BYTES = 256;
 constexpr int MAX_SLICES = 1024;
 constexpr int NCH_MAX = 64;
 
@@ -146,36 +143,47 @@ pi_status pred_l1_bt(const pi_predictor* p, const void* x, int B, float* u, hipS
 
 template <int WT, int BT>
 pi_status launch_pred_l2(const pi_predictor* p, const float* u, int B, uint64_t* mask, float* logits,
-                         int fuse, Lists L, unsigned* ctr, hipStream_t s) {
+                         hipStream_t s) {
     const int grid = (p->n + 63) / 64;
     return launch(PI_K_PRED_L2, k_pred_l2<WT, BT>, dim3(grid), dim3(THREADS),
                   (size_t)BT * p->r * sizeof(float), s, (const uint8_t*)p->P2t, p->b2,
-                  p->threshold, u, p->n, p->r, B, mask, logits, fuse, L, ctr);
+                  p->threshold, u, p->n, p->r, B, mask, logits);
 }
 
 template <int WT>
 pi_status pred_l2_bt(const pi_predictor* p, const float* u, int B, uint64_t* mask, float* logits,
-                     int fuse, Lists L, unsigned* ctr, hipStream_t s) {
+                     hipStream_t s) {
     switch (batch_tile(B)) {
-    case 1: return launch_pred_l2<WT, 1>(p, u, B, mask, logits, fuse, L, ctr, s);
-    case 2: return launch_pred_l2<WT, 2>(p, u, B, mask, logits, fuse, L, ctr, s);
-    case 4: return launch_pred_l2<WT, 4>(p, u, B, mask, logits, fuse, L, ctr, s);
-    default: return launch_pred_l2<WT, 8>(p, u, B, mask, logits, fuse, L, ctr, s);
+    case 1: return launch_pred_l2<WT, 1>(p, u, B, mask, logits, s);
+    case 2: return launch_pred_l2<WT, 2>(p, u, B, mask, logits, s);
+    case 4: return launch_pred_l2<WT, 4>(p, u, B, mask, logits, s);
+    default: return launch_pred_l2<WT, 8>(p, u, B, mask, logits, s);
     }
 }
+
+// x is staged in LDS by k_up when a token group of it fits in 64 KiB
+constexpr size_t XLDS_MAX = 65536;
 
 template <int WT, int XT, int BT, int ACT>
 pi_status launch_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
     int grid = (rows_cap + NWAVES - 1) / NWAVES;
     if (grid > 2048) grid = 2048;
     if (grid < 1) grid = 1;
-    return launch(PI_K_UP, k_up<WT, XT, BT, ACT>, dim3(grid), dim3(THREADS), 0, s, a);
+    const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
+    if (xbytes <= XLDS_MAX)
+        return launch(PI_K_UP, k_up<WT, XT, BT, ACT, true>, dim3(grid), dim3(THREADS), xbytes, s, a);
+    return launch(PI_K_UP, k_up<WT, XT, BT, ACT, false>, dim3(grid), dim3(THREADS), 0, s, a);
 }
 
 template <int WT, int BT>
 pi_status launch_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     const int slices = (a.d + Down<WT>::COLS - 1) / Down<WT>::COLS;
-    return launch(PI_K_DOWN, k_down<WT, BT>, dim3(slices, o.nch), dim3(THREADS), 0, s, a, o);
+    pi_status st = launch(PI_K_DOWN, k_down<WT, BT>, dim3(slices, o.nch), dim3(THREADS), 0, s, a, o);
+    if (st != PI_OK) return st;
+    const int64_t len = (int64_t)a.B * a.d;
+    int grid = (int)((len + THREADS - 1) / THREADS);
+    if (grid > 2048) grid = 2048;
+    return launch(PI_K_REDUCE, k_reduce, dim3(grid), dim3(THREADS), 0, s, a, o);
 }
 
 template <int WT, int XT, int BT>
@@ -259,7 +267,6 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.h_ld = n > 0 ? n : 1;
     DownOut o{};
     o.partials = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * n * 4));
-    o.ctr = reinterpret_cast<unsigned*>(base) + CTR_SLICE;
     o.y_part[0] = y0;
     o.y_part[1] = y1;
     o.y = y;
@@ -292,7 +299,7 @@ const char* pi_last_error(void) { return g_err; }
 
 const char* pi_kernel_name(int32_t kid) {
     static const char* names[PI_K_COUNT] = {"k_pred_l1", "k_pred_l2", "k_compact", "k_up", "k_down",
-                                            "k_merge", "k_profile", "k_index", "k_copy"};
+                                            "k_merge", "k_profile", "k_index", "k_copy", "k_reduce"};
     return (kid >= 0 && kid < PI_K_COUNT) ? names[kid] : "?";
 }
 
@@ -341,7 +348,6 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
     TRY(check_ws(ws, ws_bytes, ws_pred_bytes(p->r, B)));
     uint8_t* base = static_cast<uint8_t*>(ws);
     float* u = reinterpret_cast<float*>(base + WS_CTR_BYTES);
-    unsigned* ctr = reinterpret_cast<unsigned*>(base) + CTR_PRED;
     hipStream_t s = (hipStream_t)stream;
     const int wt = p->wdtype;
     pi_status st;
@@ -350,9 +356,9 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
     else
         st = xdtype == F32 ? pred_l1_bt<F16, F32>(p, x, B, u, s) : pred_l1_bt<F16, F16>(p, x, B, u, s);
     TRY(st);
-    const int fuse = lists ? 1 : 0;
-    return wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, fuse, L, ctr, s)
-                     : pred_l2_bt<F16>(p, u, B, mask, logits, fuse, L, ctr, s);
+    TRY(wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, s) : pred_l2_bt<F16>(p, u, B, mask, logits, s));
+    if (!lists) return PI_OK;
+    return launch(PI_K_COMPACT, k_compact, dim3(1), dim3(THREADS), 0, s, (const uint64_t*)mask, p->n, L);
 }
 
 pi_status pi_compact_active(const uint64_t* mask, int32_t n, const pi_active_lists* lists,

@@ -1,15 +1,17 @@
 // pi_kernels.h -- HIP kernels of the predictor-gated sparse FFN (gfx950).
 //
-// One decode layer step runs four kernels on one stream, with the active
+// One decode layer step runs six kernels on one stream, with the active
 // counts kept in device memory so the host never waits inside a step:
 //   k_pred_l1   u = ReLU(P1t x)                       (dense rows of P1t)
-//   k_pred_l2   logit = P2t u + b2, > threshold, OR over tokens -> mask words;
-//               its last workgroup compacts the mask into hot/cold lists
+//   k_pred_l2   logit = P2t u + b2, > threshold, OR over tokens -> mask words
+//   k_compact   mask -> ascending hot / cold lists + device counts
 //   k_up        gathered rows of W_up (and W_gate) -> h per active neuron
 //   k_down      gathered rows of W_downT scaled by h, 2-D tiled over
-//               (column slice x neuron chunk); the last chunk of each slice
-//               reduces the chunk partials in a fixed order into y_hot,
-//               y_cold and y = y_hot + y_cold (the merge)
+//               (column slice x neuron chunk) -> chunk partials
+//   k_reduce    chunk partials summed in a fixed order into y_hot, y_cold
+//               and y = y_hot + y_cold (the merge)
+// No kernel synchronises with another workgroup: kernel boundaries order the
+// steps, so no device-scope cache write-back is needed inside a kernel.
 // Method: PowerInfer pages -- CSDN article, sections on sparse activation
 // (predict, then compute only predicted neurons) and on the hybrid design
 // (per-partition computation of the predicted neurons, then a merge).
@@ -86,7 +88,7 @@ struct Lists {
     int32_t* counts;
 };
 
-__device__ void compact_block(const uint64_t* mask, int n, Lists L, bool coherent) {
+__device__ void compact_block(const uint64_t* mask, int n, Lists L) {
     __shared__ int s_tot[THREADS];
     __shared__ int s_hot[THREADS];
     const int words = (n + 63) / 64;
@@ -96,7 +98,7 @@ __device__ void compact_block(const uint64_t* mask, int n, Lists L, bool coheren
     const uint64_t tail = (n % 64) ? ((1ull << (n % 64)) - 1ull) : ~0ull;
     int tot = 0, hot = 0;
     for (int w = w0; w < w1; ++w) {
-        uint64_t v = coherent ? load_coherent(mask + w) : mask[w];
+        uint64_t v = mask[w];
         if (w == words - 1) v &= tail;
         tot += __popcll(v);
         int lo = 64 * w;
@@ -119,7 +121,7 @@ __device__ void compact_block(const uint64_t* mask, int n, Lists L, bool coheren
     const int T = s_tot[THREADS - 1];
     int pos = s_tot[threadIdx.x] - tot;
     for (int w = w0; w < w1; ++w) {
-        uint64_t v = coherent ? load_coherent(mask + w) : mask[w];
+        uint64_t v = mask[w];
         if (w == words - 1) v &= tail;
         while (v) {
             int bit = __builtin_ctzll(v);
@@ -138,28 +140,25 @@ __device__ void compact_block(const uint64_t* mask, int n, Lists L, bool coheren
 
 __global__ __launch_bounds__(THREADS) void k_compact(const uint64_t* __restrict__ mask, int n,
                                                      Lists L) {
-    compact_block(mask, n, L, false);
+    compact_block(mask, n, L);
 }
 
 // ===========================================================================
 // Predictor, second layer + threshold + union over tokens, one mask word (64
 // neurons) per workgroup.  Each wave owns 16 rows of P2t; 16 lanes share a row
 // (4 rows per load instruction, 256 contiguous bytes per row).  u is staged in
-// LDS per token group.  With `fuse`, the last workgroup to finish compacts the
-// whole mask into the active lists.
+// LDS per token group.
 // ===========================================================================
 template <int WT, int BT>
 __global__ __launch_bounds__(THREADS) void k_pred_l2(const uint8_t* __restrict__ P2t,
                                                      const float* __restrict__ b2, float thr,
                                                      const float* __restrict__ u, int n, int r,
                                                      int B, uint64_t* __restrict__ mask,
-                                                     float* __restrict__ logits, int fuse, Lists L,
-                                                     unsigned* ctr) {
+                                                     float* __restrict__ logits) {
     constexpr int EPC = Chunk<WT>::EPC;
     constexpr int G = 16;                       // lanes per row
     extern __shared__ float s_u[];              // [BT][r]
     __shared__ unsigned s_flag[64];
-    __shared__ int s_last;
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     const int gi = lane / G, li = lane % G;
     const int nch = r / EPC;
@@ -217,15 +216,6 @@ __global__ __launch_bounds__(THREADS) void k_pred_l2(const uint8_t* __restrict__
         uint64_t word = __ballot(i < n && s_flag[lane] != 0);
         if (lane == 0) mask[blockIdx.x] = word;
     }
-    if (!fuse) return;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = arrive(ctr) == gridDim.x - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    compact_block(mask, n, L, true);
-    if (threadIdx.x == 0) reset_counter(ctr);
 }
 
 // ===========================================================================
@@ -273,61 +263,80 @@ __device__ __forceinline__ void item_row(const FfnArgs& a, int item, int H, int&
     }
 }
 
-// Up/gate: one wave per item; lanes stride over the row's chunks, U chunks in
-// flight per lane; the wave reduces; lane 0 applies bias and activation.
-template <int WT, int XT, int BT, int ACT>
+// Up/gate: one wave per item; lanes stride over the row's 16-byte chunks with U
+// chunks in flight per lane; the wave reduces; lane 0 applies bias and
+// activation.  x is staged in LDS when BT*d fits (XLDS), so x reads do not
+// queue behind the weight stream; item and row ids are wave-uniform (scalar).
+// Batches are branch-free: chunks past the row end are clamped and dropped.
+template <int WT, int XT, int BT, int ACT, bool XLDS>
 __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
     constexpr int EPC = Chunk<WT>::EPC;
     constexpr int XB = XT == F32 ? 4 : 2;
     constexpr int U = WT == Q4 ? 4 : 8;
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];   // [BT][d] when XLDS
     const int lane = threadIdx.x & (WAVE - 1);
-    const int gw = (blockIdx.x * THREADS + threadIdx.x) / WAVE;
+    const int gw = __builtin_amdgcn_readfirstlane((blockIdx.x * THREADS + threadIdx.x) / WAVE);
     const int nw = gridDim.x * NWAVES;
     int H, C;
     item_counts(a, H, C);
     const int T = H + C;
     const int nch = a.d / EPC;
-    for (int item = gw; item < T; item += nw) {
-        int part, row;
-        item_row(a, item, H, part, row);
-        if ((unsigned)row >= (unsigned)a.rows[part]) {     // id outside the partition: h = 0
-            if (lane == 0)
-                for (int b = 0; b < a.B; ++b) a.h[(int64_t)b * a.h_ld + item] = 0.0f;
-            continue;
+    const int64_t xrow = (int64_t)a.d * XB;
+    for (int b0 = 0; b0 < a.B; b0 += BT) {
+        const int nb = min(BT, a.B - b0);
+        if (XLDS) {
+            __syncthreads();
+            const u4* src = reinterpret_cast<const u4*>(a.x + b0 * xrow);
+            u4* dst = reinterpret_cast<u4*>(s_x);
+            const int n16 = (int)(nb * xrow / 16), all16 = (int)(BT * xrow / 16);
+            for (int k = threadIdx.x; k < all16; k += THREADS)
+                dst[k] = k < n16 ? src[k] : u4{0u, 0u, 0u, 0u};
+            __syncthreads();
         }
-        const uint8_t* wu = a.up[part] + (int64_t)row * a.rb;
-        const uint8_t* wg = ACT == REGLU ? a.gate[part] + (int64_t)row * a.rb : nullptr;
-        for (int b0 = 0; b0 < a.B; b0 += BT) {
+        const uint8_t* xg = XLDS ? s_x : a.x + b0 * xrow;
+        for (int item = gw; item < T; item += nw) {
+            int part, row;
+            item_row(a, item, H, part, row);
+            if ((unsigned)row >= (unsigned)a.rows[part]) {     // id outside the partition: h = 0
+                if (lane == 0)
+                    for (int b = 0; b < nb; ++b) a.h[(int64_t)(b0 + b) * a.h_ld + item] = 0.0f;
+                continue;
+            }
+            const uint8_t* wu = a.up[part] + (int64_t)row * a.rb;
+            const uint8_t* wg = ACT == REGLU ? a.gate[part] + (int64_t)row * a.rb : nullptr;
             float au[BT], ag[BT];
 #pragma unroll
             for (int b = 0; b < BT; ++b) au[b] = ag[b] = 0.0f;
             for (int c0 = lane; c0 < nch; c0 += WAVE * U) {
                 u4 vu[U], vg[U];
                 float su[U], sg[U];
+                int cq[U];
 #pragma unroll
-                for (int k = 0; k < U; ++k) {
-                    const int c = c0 + WAVE * k;
-                    if (c < nch) {
-                        vu[k] = ld16_stream(wu + 16 * (int64_t)c);
-                        su[k] = WT == Q4 ? half_f(*(const uint16_t*)(wu + a.d / 2 + 2 * c)) : 0.f;
-                        if (ACT == REGLU) {
-                            vg[k] = ld16_stream(wg + 16 * (int64_t)c);
-                            sg[k] = WT == Q4 ? half_f(*(const uint16_t*)(wg + a.d / 2 + 2 * c))
-                                             : 0.f;
-                        }
-                    }
+                for (int q = 0; q < U; ++q) cq[q] = min(c0 + WAVE * q, nch - 1);
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    vu[q] = ld16_stream(wu + 16 * (int64_t)cq[q]);
+                    if (ACT == REGLU) vg[q] = ld16_stream(wg + 16 * (int64_t)cq[q]);
                 }
 #pragma unroll
-                for (int k = 0; k < U; ++k) {
-                    const int c = c0 + WAVE * k;
-                    if (c < nch) {
+                for (int q = 0; q < U; ++q) {
+                    su[q] = WT == Q4 ? half_f(*(const uint16_t*)(wu + a.d / 2 + 2 * cq[q])) : 0.f;
+                    if (ACT == REGLU)
+                        sg[q] = WT == Q4 ? half_f(*(const uint16_t*)(wg + a.d / 2 + 2 * cq[q])) : 0.f;
+                }
 #pragma unroll
-                        for (int b = 0; b < BT; ++b) {
-                            if (b0 + b < a.B) {
-                                const uint8_t* xp = a.x + ((int64_t)(b0 + b) * a.d + c * EPC) * XB;
-                                au[b] = Dot<WT, XT>::run(vu[k], su[k], xp, au[b]);
-                                if (ACT == REGLU) ag[b] = Dot<WT, XT>::run(vg[k], sg[k], xp, ag[b]);
-                            }
+                for (int q = 0; q < U; ++q) {
+                    const bool valid = c0 + WAVE * q < nch;
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) {
+                        // token slots past B read token nb-1 (in bounds) and are dropped
+                        const uint8_t* xp = xg + (b < nb ? b : nb - 1) * xrow +
+                                            (int64_t)cq[q] * EPC * XB;
+                        const float tu = Dot<WT, XT>::run(vu[q], su[q], xp, 0.0f);
+                        au[b] += valid ? tu : 0.0f;
+                        if (ACT == REGLU) {
+                            const float tg = Dot<WT, XT>::run(vg[q], sg[q], xp, 0.0f);
+                            ag[b] += valid ? tg : 0.0f;
                         }
                     }
                 }
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
             for (int b = 0; b < BT; ++b) {
                 float up = wave_sum(au[b]);
                 float g = ACT == REGLU ? wave_sum(ag[b]) : 0.0f;
-                if (lane == 0 && b0 + b < a.B) {
+                if (lane == 0 && b < nb) {
                     up += a.bup[part] ? a.bup[part][row] : 0.0f;
                     float hv;
                     if (ACT == RELU) {
@@ -355,11 +364,10 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
 // Down: grid (column slices, neuron chunks).  Chunks are split between the
 // partitions in proportion to their active counts so no chunk mixes them.
 // Each wave walks the chunk's items with stride NWAVES, U rows in flight; the
-// four waves reduce through LDS; the chunk writes its partial; the last chunk
-// of the slice sums the partials in chunk order into y_hot / y_cold / y.
+// four waves reduce through LDS; the chunk writes its partial; k_reduce then
+// sums the partials in chunk order into y_hot / y_cold / y.
 struct DownOut {
     float* partials;    // [nch][B][d]
-    unsigned* ctr;      // [slices]
     float* y_part[2];   // [B][d] or NULL
     float* y;           // [B][d] or NULL
     int nch;
@@ -387,20 +395,27 @@ template <int WT, int BT>
 __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
     using D = Down<WT>;
     constexpr int DCH = D::DCH;
-    constexpr int U = 8;
+    constexpr int U = 8;              // rows in flight per wave
+    constexpr int STAGE = 256;        // rows whose ids and h are staged in LDS at a time
     __shared__ float s_red[NWAVES - 1][DCH][WAVE];
-    __shared__ int s_last;
-    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    __shared__ int s_row[STAGE];
+    __shared__ float s_h[BT][STAGE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int slice = blockIdx.x, k = blockIdx.y;
     // this lane's first column: lanes cover D::COLS consecutive columns
     const int lane_col = WT == Q4 ? 32 * (lane >> 1) + 8 * (lane & 1) : lane * DCH;
     const int col0 = slice * D::COLS + lane_col;
     const bool active_col = col0 < a.d;
+    const int colL = active_col ? col0 : 0;   // lanes past d read column 0, drop the result
     int H, C;
     item_counts(a, H, C);
     int part, lo, hi, nh;
     chunk_range(o.nch, H, C, k, part, lo, hi, nh);
     const int hbase = part == 0 ? 0 : H;
+    const uint8_t* base = part == 0 ? a.down[0] : a.down[1];
+    const int32_t* idx = part == 0 ? a.idx[0] : a.idx[1];
+    const int prow_max = part == 0 ? a.rows[0] : a.rows[1];
     const int B = a.B;
     for (int b0 = 0; b0 < B; b0 += BT) {
         float acc[BT][DCH];
@@ -408,27 +423,35 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
         for (int b = 0; b < BT; ++b)
 #pragma unroll
             for (int e = 0; e < DCH; ++e) acc[b][e] = 0.0f;
-        for (int it0 = lo + wv; it0 < hi; it0 += NWAVES * U) {
-            typename D::raw w[U];
-            float hv[U][BT];
+        for (int s0 = lo; s0 < hi; s0 += STAGE) {
+            const int len = min(STAGE, hi - s0);
+            __syncthreads();                  // the previous stage is consumed
+            for (int t = threadIdx.x; t < len; t += THREADS) {
+                int row = idx ? idx[s0 + t] : s0 + t;
+                if ((unsigned)row >= (unsigned)prow_max) row = 0;   // k_up gave it h = 0
+                s_row[t] = row;
 #pragma unroll
-            for (int q = 0; q < U; ++q) {
-                const int it = it0 + NWAVES * q;
-                if (it < hi) {
-                    int row = a.idx[part] ? a.idx[part][it] : it;
-                    if ((unsigned)row >= (unsigned)a.rows[part]) row = 0;   // its h is 0
-                    if (active_col) w[q] = D::load(a.down[part] + (int64_t)row * a.rb, a.d, col0);
-#pragma unroll
-                    for (int b = 0; b < BT; ++b)
-                        hv[q][b] = b0 + b < B ? a.h[(int64_t)(b0 + b) * a.h_ld + hbase + it] : 0.f;
-                }
+                for (int b = 0; b < BT; ++b)
+                    s_h[b][t] = b0 + b < B ? a.h[(int64_t)(b0 + b) * a.h_ld + hbase + s0 + t] : 0.f;
             }
+            __syncthreads();
+            // ids come from LDS and the batch is branch-free (rows past the stage are
+            // clamped and weighted by 0), so the U weight loads issue back to back
+            for (int t0 = wv; t0 < len; t0 += NWAVES * U) {
+                typename D::raw w[U];
+                int tq[U];
 #pragma unroll
-            for (int q = 0; q < U; ++q) {
-                const int it = it0 + NWAVES * q;
-                if (it < hi && active_col) {
+                for (int q = 0; q < U; ++q) tq[q] = min(t0 + NWAVES * q, len - 1);
 #pragma unroll
-                    for (int b = 0; b < BT; ++b) D::axpy(w[q], hv[q][b], acc[b]);
+                for (int q = 0; q < U; ++q) {
+                    const int row = __builtin_amdgcn_readfirstlane(s_row[tq[q]]);
+                    w[q] = D::load(base + (int64_t)row * a.rb, a.d, colL);
+                }
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const bool valid = t0 + NWAVES * q < len;
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) D::axpy(w[q], valid ? s_h[b][tq[q]] : 0.0f, acc[b]);
                 }
             }
         }
@@ -455,28 +478,26 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
             }
         }
     }
-    // the last chunk of this slice reduces the partials in chunk order
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = arrive(o.ctr + slice) == (unsigned)o.nch - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int c0 = slice * D::COLS;
-    const int ncols = min(D::COLS, a.d - c0);
-    for (int t = threadIdx.x; t < ncols * B; t += THREADS) {
-        const int b = t / ncols, c = c0 + t % ncols;
+}
+
+// Reduction of the chunk partials, one thread per output element: the hot
+// chunks in order give y_hot, the cold chunks in order give y_cold, and
+// y = y_hot + y_cold is the merge.  Deterministic (fixed order, no atomics).
+__global__ __launch_bounds__(THREADS) void k_reduce(FfnArgs a, DownOut o) {
+    int H, C;
+    item_counts(a, H, C);
+    int part, lo, hi, nh;
+    chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
+    const int64_t len = (int64_t)a.B * a.d;
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t at = (int64_t)blockIdx.x * THREADS + threadIdx.x; at < len; at += stride) {
         float yh = 0.0f, yc = 0.0f;
-        for (int kk = 0; kk < nh; ++kk)
-            yh += load_coherent(o.partials + ((int64_t)kk * B + b) * a.d + c);
-        for (int kk = nh; kk < o.nch; ++kk)
-            yc += load_coherent(o.partials + ((int64_t)kk * B + b) * a.d + c);
-        const int64_t at = (int64_t)b * a.d + c;
+        for (int kk = 0; kk < nh; ++kk) yh += o.partials[kk * len + at];
+        for (int kk = nh; kk < o.nch; ++kk) yc += o.partials[kk * len + at];
         if (o.y_part[0]) o.y_part[0][at] = yh;
         if (o.y_part[1]) o.y_part[1][at] = yc;
         if (o.y) o.y[at] = yh + yc;
     }
-    if (threadIdx.x == 0) reset_counter(o.ctr + slice);
 }
 
 // ===========================================================================
