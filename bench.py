@@ -1,10 +1,11 @@
 """Benchmark of the predictor-gated sparse FFN decode step on one MI355X.
 
 One step = one pass of the whole hot path over one token batch: predictor
-(both layers, threshold, union) and compaction into hot/cold lists
-(`pi_predict` with lists), then the sparse FFN over the hot and the cold
-partition with the merge fused into the reduction of the down projection's
-partials (`pi_sparse_ffn_split`).  Six kernels, no host synchronisation.
+(both layers, threshold, union -> mask; `pi_predict`), then
+`pi_sparse_ffn_split` with the mask: compaction into hot/cold lists fused into
+the up/gate kernel, the sparse FFN over the hot and the cold partition, and
+the merge fused into the reduction of the down projection's partials.  Five
+kernels, no host synchronisation.
 
 Default workload: the OPT-30B-shaped ReLU layer (d_model 7168, d_ffn 28672,
 predictor rank 1024, fp16 weights, fp32 accumulation, batch 1), hot partition
@@ -63,6 +64,7 @@ def kernel_bytes(wl, B, active):
         "k_compact": 8 * words + 4 * active + 8,
         "k_up": active * (m_up * wrow_bytes(wl) + 4 + 4) + B * wl.d * ex + 4 * B * active,
         "k_down": active * (wrow_bytes(wl) + 4) + 4 * B * active,
+        "k_ffn": active * (m_up * wrow_bytes(wl) + wrow_bytes(wl) + 4) + B * wl.d * ex,
         "k_reduce": 4 * B * wl.d,
     }
 
@@ -105,6 +107,8 @@ def main():
     ap.add_argument("--instances", type=int, default=INSTANCES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of a captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the sparse FFN is a single-GPU path here "
@@ -143,27 +147,43 @@ def main():
     def step(i):
         pred, (hot, cold) = descs[i % len(layers)]
         x = xs[i]
-        pb.pi_predict(pred, x, buf.mask, None, buf.lists, buf.ws)
-        pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, None, None, buf.y, buf.ws)
+        pb.pi_predict(pred, x, buf.mask, None, None, buf.ws)
+        pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, None, None, buf.y, buf.ws, mask=buf.mask)
 
     log(f"[bench] warmup {W} + timed {K} steps over {len(layers)} instances ...")
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager launches from Python: host-bound for kernels this short (reported aside)
     e0.record()
     for i in range(W, W + K):
         step(i)
     e1.record()
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    us_step = ms_total * 1e3 / K
+    us_step_eager = e0.elapsed_time(e1) * 1e3 / K
+    # the timed steps captured once into a HIP graph and replayed: device time only
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(W, W + K):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us_step = e0.elapsed_time(e1) * 1e3 / K
+    else:
+        us_step = us_step_eager
 
     # second pass over the same steps: per-kernel durations from dispatch events, and the
     # active count of each step (deterministic, so identical to the first pass)
     kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2,
             "k_compact": pb.PI_K_COMPACT, "k_up": pb.PI_K_UP, "k_down": pb.PI_K_DOWN,
-            "k_reduce": pb.PI_K_REDUCE}
+            "k_ffn": pb.PI_K_FFN, "k_reduce": pb.PI_K_REDUCE}
     for kid in kids.values():
         pb.pi_kernel_timer_start(kid, K)
     active = []
@@ -226,11 +246,13 @@ def main():
                    "hot_fraction": wl.hot_frac, "n_hot": n_hot, "instances": len(layers),
                    "mean_active": round(mean_active, 1),
                    "mean_hot_active": round(float(np.mean(hot_active)), 1)},
+        "timing": "eager" if args.eager else "hip_graph",
+        "us_per_step_eager_launch": round(us_step_eager, 3),
         "touched_bytes_per_step": round(touched),
         "achieved_gbps_touched": round(gbps_touched, 1),
         "frac_of_peak_touched": round(gbps_touched / PEAK_HBM_GBPS, 4),
-        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "kernel_bytes": {k: round(v) for k, v in kb_mean.items()},
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items() if kern_ms[k][1] > 0},
+        "kernel_bytes": {k: round(kb_mean[k]) for k in kern_us if kern_ms[k][1] > 0},
         "roofline": roofline, "dense_ffn": dense, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -165,14 +165,19 @@ pi_status pi_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32
 /*
  * Sparse FFN over the hot and the cold partition in one pass, with the merge
  * fused: y_hot and y_cold receive the two partial outputs (each may be NULL),
- * y receives y_hot + y_cold (may be NULL).  `lists` comes from pi_predict or
- * pi_compact_active with lists->n_hot == hot->rows.  cold may be NULL (or
- * have 0 rows) when there is no cold partition.  Both partitions need the
- * same d, wdtype and act.
+ * y receives y_hot + y_cold (may be NULL).  cold may be NULL (or have 0
+ * rows) when there is no cold partition.  Both partitions need the same d,
+ * wdtype and act, and lists->n_hot == hot->rows.
+ *   mask NULL:  the active set is `lists` as given (from pi_predict or
+ *               pi_compact_active), an input.
+ *   mask given: the active set is mask [ceil(n/64)] (n = hot rows + cold
+ *               rows, from pi_predict); the compaction is fused into this
+ *               call and `lists` (ids, counts) are outputs, identical to
+ *               what pi_compact_active would write.
  */
 pi_status pi_sparse_ffn_split(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
-                              int32_t B, int32_t xdtype, const pi_active_lists* lists,
-                              float* y_hot, float* y_cold, float* y,
+                              int32_t B, int32_t xdtype, const uint64_t* mask,
+                              const pi_active_lists* lists, float* y_hot, float* y_cold, float* y,
                               void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -238,8 +243,9 @@ enum {
     PI_K_PROFILE = 6,
     PI_K_INDEX = 7,
     PI_K_COPY = 8,
-    PI_K_REDUCE = 9,      /* chunk partials -> y_hot, y_cold, y (fused merge) */
-    PI_K_COUNT = 10
+    PI_K_REDUCE = 9,      /* partials of y -> y_hot, y_cold, y (fused merge) */
+    PI_K_FFN = 10,        /* fused compaction + up/gate + activation + down (batch <= 4) */
+    PI_K_COUNT = 11
 };
 
 /*

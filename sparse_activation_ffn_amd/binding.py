@@ -21,7 +21,7 @@ PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
 PI_RELU, PI_REGLU = 0, 1
 PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
- PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_COUNT) = range(11)
+ PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_COUNT) = range(12)
 
 # every symbol include/pi.h declares
 EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_active",
@@ -73,7 +73,7 @@ def lib() -> C.CDLL:
         "pi_predict": ([P, P, I32, I32, P, P, P, P, SZ, P], I32),
         "pi_compact_active": ([P, I32, P, P], I32),
         "pi_sparse_ffn": ([P, P, I32, I32, P, P, P, P, SZ, P], I32),
-        "pi_sparse_ffn_split": ([P, P, P, I32, I32, P, P, P, P, P, SZ, P], I32),
+        "pi_sparse_ffn_split": ([P, P, P, I32, I32, P, P, P, P, P, P, SZ, P], I32),
         "pi_merge": ([P, P, I32, I32, P, P], I32),
         "pi_dense_ffn": ([P, P, I32, I32, P, P, SZ, P], I32),
         "pi_profile_counts": ([P, P, I32, I32, P, P], I32),
@@ -157,9 +157,10 @@ def pi_sparse_ffn(part: FfnPart, x, idx, count, y, ws, stream=None):
 
 
 def pi_sparse_ffn_split(hot: FfnPart, cold: Optional[FfnPart], x, lists: ActiveLists,
-                        y_hot=None, y_cold=None, y=None, ws=None, stream=None):
+                        y_hot=None, y_cold=None, y=None, ws=None, stream=None, mask=None):
+    """mask given: compaction fused, `lists` are outputs; mask None: `lists` are inputs."""
     _check(lib().pi_sparse_ffn_split(C.byref(hot), None if cold is None else C.byref(cold),
-                                     ptr(x), x.shape[0], dtype_code(x), C.byref(lists),
+                                     ptr(x), x.shape[0], dtype_code(x), ptr(mask), C.byref(lists),
                                      ptr(y_hot), ptr(y_cold), ptr(y), ptr(ws),
                                      0 if ws is None else ws.numel() * ws.element_size(),
                                      stream_handle(stream)))

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "pi.h"
+#include "pi_ffn.h"
 #include "pi_kernels.h"
 
 using namespace pi;
@@ -53,10 +54,35 @@ int pick_nch(int d, int wt, int B) {
     return nch < 2 ? 2 : nch > NCH_MAX ? NCH_MAX : nch;
 }
 
+// Fused kernel (k_ffn): one workgroup per compute unit of the MI355X.
+constexpr int NWG_FUSED = 256;
+constexpr int FUSED_MAX_BATCH = 4;
+
+// 16-byte chunks per thread of k_ffn for rows of d elements (1, 2 or 4; 0 = too wide)
+int fused_nc(int d, int wt) {
+    const int epc = wt == F32 ? 4 : wt == F16 ? 8 : 32;
+    const int nc = (d / epc + FT - 1) / FT;
+    return nc <= 1 ? 1 : nc <= 2 ? 2 : nc <= 4 ? 4 : 0;
+}
+
+// The fused path takes batches up to 4 with the natural x dtype of the weights,
+// where its double-buffered rows and accumulators fit in registers (Q4_0:
+// batch 1 and d <= 16384; four chunks per thread: batch 1); other shapes take
+// the gathered two-kernel path.
+bool use_fused(int d, int wt, int xt, int B) {
+    const bool pair = (wt == F32 && xt == F32) || (wt != F32 && xt == F16);
+    const int nc = fused_nc(d, wt);
+    if (!pair || B > FUSED_MAX_BATCH || nc == 0) return false;
+    if (wt == Q4 && (B > 1 || nc == 4)) return false;
+    if (nc == 4 && B > 1) return false;
+    return true;
+}
+
 size_t ws_pred_bytes(int r, int B) { return WS_CTR_BYTES + align256((size_t)B * r * 4); }
 
-size_t ws_ffn_bytes(int d, int n, int B, int nch) {
-    return WS_CTR_BYTES + align256((size_t)B * n * 4) + align256((size_t)nch * B * d * 4);
+// h [B][n] (gathered path only) and the partials of y
+size_t ws_ffn_bytes(int d, int n, int B, int nparts) {
+    return WS_CTR_BYTES + align256((size_t)B * n * 4) + align256((size_t)nparts * B * d * 4);
 }
 
 // ---- timing hooks --------------------------------------------------------------
@@ -170,9 +196,12 @@ pi_status launch_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
     if (grid > 2048) grid = 2048;
     if (grid < 1) grid = 1;
     const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
+    const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
+    const size_t mbytes = words ? words * 8 + (words + 1) * 4 : 0;   // mask words + their scan
     if (xbytes <= XLDS_MAX)
-        return launch(PI_K_UP, k_up<WT, XT, BT, ACT, true>, dim3(grid), dim3(THREADS), xbytes, s, a);
-    return launch(PI_K_UP, k_up<WT, XT, BT, ACT, false>, dim3(grid), dim3(THREADS), 0, s, a);
+        return launch(PI_K_UP, k_up<WT, XT, BT, ACT, true>, dim3(grid), dim3(THREADS),
+                      xbytes + mbytes, s, a);
+    return launch(PI_K_UP, k_up<WT, XT, BT, ACT, false>, dim3(grid), dim3(THREADS), mbytes, s, a);
 }
 
 template <int WT, int BT>
@@ -204,6 +233,59 @@ pi_status ffn_bt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipS
     }
 }
 
+// ---- fused path -------------------------------------------------------------
+template <typename K>
+pi_status allow_lds(K kernel, size_t bytes) {
+    if (bytes <= 65536) return PI_OK;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return fail(PI_ERR_HIP, "LDS attribute: %s", hipGetErrorString(e));
+    return PI_OK;
+}
+
+template <int WT, int XT, int BT, int ACT, int NC>
+pi_status launch_fused(const FfnArgs& a, const DownOut& o, hipStream_t s) {
+    const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
+    const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
+    const size_t sh = xbytes + (words ? words * 8 + (words + 1) * 4 : 0);
+    auto kern = k_ffn<WT, XT, BT, ACT, NC>;
+    TRY(allow_lds(kern, sh));
+    TRY(launch(PI_K_FFN, kern, dim3(o.nch), dim3(FT), sh, s, a, o));
+    const int64_t len = (int64_t)a.B * a.d;
+    return launch(PI_K_REDUCE, k_reduce_parts, dim3((unsigned)((len + RE - 1) / RE)),
+                  dim3(RE * RS), 0, s, a, o);
+}
+
+template <int WT, int XT, int BT, int ACT>
+pi_status fused_nc_dispatch(const FfnArgs& a, const DownOut& o, hipStream_t s) {
+    switch (fused_nc(a.d, WT)) {
+    case 1: return launch_fused<WT, XT, BT, ACT, 1>(a, o, s);
+    case 2: return launch_fused<WT, XT, BT, ACT, 2>(a, o, s);
+    default: return launch_fused<WT, XT, BT, ACT, 4>(a, o, s);
+    }
+}
+
+template <int WT, int XT, int BT>
+pi_status fused_act(const FfnArgs& a, const DownOut& o, int act, hipStream_t s) {
+    return act == PI_RELU ? fused_nc_dispatch<WT, XT, BT, RELU>(a, o, s)
+                          : fused_nc_dispatch<WT, XT, BT, REGLU>(a, o, s);
+}
+
+template <int WT, int XT>
+pi_status fused_bt(const FfnArgs& a, const DownOut& o, int act, hipStream_t s) {
+    switch (batch_tile(a.B)) {
+    case 1: return fused_act<WT, XT, 1>(a, o, act, s);
+    case 2: return fused_act<WT, XT, 2>(a, o, act, s);
+    default: return fused_act<WT, XT, 4>(a, o, act, s);
+    }
+}
+
+pi_status run_fused(const FfnArgs& a, const DownOut& o, int wt, int act, hipStream_t s) {
+    if (wt == F32) return fused_bt<F32, F32>(a, o, act, s);
+    if (wt == F16) return fused_bt<F16, F16>(a, o, act, s);
+    return fused_act<Q4, F16, 1>(a, o, act, s);          // Q4_0: batch 1 only (use_fused)
+}
+
 pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, int rows_cap,
                   hipStream_t s) {
     if (wt == F32) return xt == F32 ? ffn_bt<F32, F32>(a, o, act, rows_cap, s) : ffn_bt<F32, F16>(a, o, act, rows_cap, s);
@@ -212,10 +294,12 @@ pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, i
 }
 
 // Shared body of pi_sparse_ffn / pi_sparse_ffn_split / pi_dense_ffn.
+// mask != NULL: the active set is read from mask words and the lists (idx0,
+// idx1, counts) are outputs, written by k_up; otherwise they are inputs.
 pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x, int B,
-                     int xdtype, const int32_t* idx0, const int32_t* idx1, const int32_t* counts,
-                     bool dense, float* y0, float* y1, float* y, void* ws, size_t ws_bytes,
-                     hipStream_t s) {
+                     int xdtype, const uint64_t* mask, const int32_t* idx0, const int32_t* idx1,
+                     const int32_t* counts, bool dense, float* y0, float* y1, float* y, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
     TRY(check_part(hot, "hot", !dense));
     const bool has_cold = cold && cold->rows > 0;
     if (cold) TRY(check_part(cold, "cold", true));
@@ -235,7 +319,8 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     }
     const int d = hot->d, wt = hot->wdtype;
     const int n = hot->rows + (has_cold ? cold->rows : 0);
-    const int nch = pick_nch(d, wt, B);
+    const bool fused = use_fused(d, wt, xdtype, B);
+    const int nch = fused ? NWG_FUSED : pick_nch(d, wt, B);
     TRY(check_ws(ws, ws_bytes, ws_ffn_bytes(d, n, B, nch)));
 
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -258,6 +343,20 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.nparts = has_cold ? 2 : 1;
     a.rows[0] = hot->rows;
     a.rows[1] = has_cold ? cold->rows : 0;
+    if (mask) {
+        CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
+        Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),
+                const_cast<int32_t*>(counts)};
+        if ((n + 63) / 64 <= MASK_WORDS_MAX) {
+            a.mask = mask;                   // compaction fused into k_up
+            a.n = n;
+            a.out_idx[0] = L.hot;
+            a.out_idx[1] = L.cold;
+            a.out_counts = L.counts;
+        } else {
+            TRY(launch(PI_K_COMPACT, k_compact, dim3(1), dim3(THREADS), 0, s, mask, n, L));
+        }
+    }
     a.dense_rows = dense ? hot->rows : 0;
     a.d = d;
     a.B = B;
@@ -271,6 +370,7 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     o.y_part[1] = y1;
     o.y = y;
     o.nch = nch;
+    if (fused) return run_fused(a, o, wt, hot->act, s);
     return run_ffn(a, o, wt, xdtype, hot->act, n, s);
 }
 
@@ -299,7 +399,8 @@ const char* pi_last_error(void) { return g_err; }
 
 const char* pi_kernel_name(int32_t kid) {
     static const char* names[PI_K_COUNT] = {"k_pred_l1", "k_pred_l2", "k_compact", "k_up", "k_down",
-                                            "k_merge", "k_profile", "k_index", "k_copy", "k_reduce"};
+                                            "k_merge", "k_profile", "k_index", "k_copy", "k_reduce",
+                                            "k_ffn"};
     return (kid >= 0 && kid < PI_K_COUNT) ? names[kid] : "?";
 }
 
@@ -309,6 +410,10 @@ size_t pi_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t B) {
     for (int wt = F32; wt <= Q4; ++wt) {
         size_t f = ws_ffn_bytes(d, n, B, pick_nch(d, wt, B));
         if (f > need) need = f;
+        if (B <= FUSED_MAX_BATCH) {
+            f = ws_ffn_bytes(d, n, B, NWG_FUSED);
+            if (f > need) need = f;
+        }
     }
     return need;
 }
@@ -381,24 +486,24 @@ pi_status pi_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32
     CHECK(count && aligned(count, 4), PI_ERR_ARG, "count required (4-byte aligned)");
     // a single partition runs as the hot half of a split with no cold part:
     // items are idx[0 .. *count) and only count[0] is read
-    return ffn_common(part, nullptr, x, B, xdtype, idx, nullptr, count, false, nullptr, nullptr,
+    return ffn_common(part, nullptr, x, B, xdtype, nullptr, idx, nullptr, count, false, nullptr, nullptr,
                       y, ws, ws_bytes, (hipStream_t)stream);
 }
 
 pi_status pi_sparse_ffn_split(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
-                              int32_t B, int32_t xdtype, const pi_active_lists* lists,
-                              float* y_hot, float* y_cold, float* y, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              int32_t B, int32_t xdtype, const uint64_t* mask,
+                              const pi_active_lists* lists, float* y_hot, float* y_cold, float* y,
+                              void* ws, size_t ws_bytes, void* stream) {
     CHECK(lists, PI_ERR_ARG, "lists required");
     CHECK(hot && lists->n_hot == hot->rows, PI_ERR_SHAPE, "lists->n_hot must equal hot->rows");
-    return ffn_common(hot, cold, x, B, xdtype, lists->hot_idx, lists->cold_idx, lists->counts,
-                      false, y_hot, y_cold, y, ws, ws_bytes, (hipStream_t)stream);
+    return ffn_common(hot, cold, x, B, xdtype, mask, lists->hot_idx, lists->cold_idx,
+                      lists->counts, false, y_hot, y_cold, y, ws, ws_bytes, (hipStream_t)stream);
 }
 
 pi_status pi_dense_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype, float* y,
                        void* ws, size_t ws_bytes, void* stream) {
     CHECK(y, PI_ERR_ARG, "y required");
-    return ffn_common(part, nullptr, x, B, xdtype, nullptr, nullptr, nullptr, true, nullptr,
+    return ffn_common(part, nullptr, x, B, xdtype, nullptr, nullptr, nullptr, nullptr, true, nullptr,
                       nullptr, y, ws, ws_bytes, (hipStream_t)stream);
 }
 

@@ -1,0 +1,331 @@
+// pi_ffn.h -- fused sparse FFN kernel for small batches (gfx950).
+//
+// One workgroup per compute unit streams whole active neurons: for a group of
+// G rows it loads the W_up (and W_gate) rows and the W_downT rows together,
+// reduces the up/gate dot products across the workgroup, applies the
+// activation, and accumulates h * W_downT[i][:] into per-thread columns.  Each
+// workgroup ends with one full-width fp32 partial of y; k_reduce_parts sums
+// the partials (hot workgroups into y_hot, cold ones into y_cold, y = y_hot +
+// y_cold).  With a mask, the compaction into ascending hot / cold lists runs
+// in the prologue of every workgroup (the mask is small and scanned in LDS),
+// and the lists are written as a side output.
+//
+// PowerInfer pages: CSDN article, section on sparse activation (only the
+// predicted neurons' rows are read and computed) and hybrid-design figure
+// (each partition computes its predicted neurons; the results are merged).
+#pragma once
+#include "pi_kernels.h"
+
+namespace pi {
+
+constexpr int FT = 512;               // threads of the fused kernel (8 waves)
+constexpr int FW = FT / WAVE;
+constexpr int FSTAGE = 256;           // item rows resolved into LDS at a time
+
+// acc[0..EPC) += h * (one 16-byte weight chunk, decoded); columns are the
+// chunk's elements in order.
+template <int WT> struct Axpy;
+template <> struct Axpy<F32> {
+    __device__ static void run(u4 w, float, float h, float* acc) {
+        acc[0] = fmaf(h, bits_f(w.x), acc[0]);
+        acc[1] = fmaf(h, bits_f(w.y), acc[1]);
+        acc[2] = fmaf(h, bits_f(w.z), acc[2]);
+        acc[3] = fmaf(h, bits_f(w.w), acc[3]);
+    }
+};
+template <> struct Axpy<F16> {
+    __device__ static void run(u4 w, float, float h, float* acc) {
+        const unsigned v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            acc[2 * m] = fmaf(h, half_lo(v[m]), acc[2 * m]);
+            acc[2 * m + 1] = fmaf(h, half_hi(v[m]), acc[2 * m + 1]);
+        }
+    }
+};
+template <> struct Axpy<Q4> {
+    // one whole block: code byte t -> element t (low nibble), t + 16 (high nibble)
+    __device__ static void run(u4 w, float s, float h, float* acc) {
+        const float hs = h * s;
+        const unsigned v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const unsigned byte = (v[t >> 2] >> (8 * (t & 3))) & 0xffu;
+            acc[t] = fmaf(hs, (float)(int)(byte & 15u) - 8.0f, acc[t]);
+            acc[16 + t] = fmaf(hs, (float)(int)(byte >> 4) - 8.0f, acc[16 + t]);
+        }
+    }
+};
+
+// Fused gathered FFN.  NC = 16-byte chunks of a row per thread (d <= NC * FT * EPC);
+// G = rows per group so a group has 8 chunks per matrix in flight per thread.
+template <int WT, int XT, int BT, int ACT, int NC>
+__global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int XB = XT == F32 ? 4 : 2;
+    // rows per group: two register buffers of G rows x NC chunks x (2 or 3 matrices)
+    // plus BT x NC x EPC accumulators must fit in 256 VGPRs
+    constexpr int G0 = (WT == Q4 ? 4 : 8) / NC / (ACT == REGLU ? 2 : 1) / (BT >= 4 ? 2 : 1);
+    constexpr int G = G0 > 0 ? G0 : 1;
+    constexpr int NM = ACT == REGLU ? 2 : 1;          // dot products per row (up, gate)
+    // dynamic LDS: [x for BT tokens] [mask words] [their popcount scan]
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+    __shared__ int s_row[FSTAGE];
+    __shared__ float s_red[2][FW][G][NM][BT];
+    const int64_t xrow = (int64_t)a.d * XB;
+    uint8_t* s_x = s_dyn;
+    const int words = a.mask ? (a.n + 63) / 64 : 0;
+    uint64_t* s_words = reinterpret_cast<uint64_t*>(s_dyn + BT * xrow);
+    int* s_scan = reinterpret_cast<int*>(s_words + words);
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wv = tid / WAVE;
+    const int nch = a.d / EPC;                         // 16-byte (code) chunks of a row
+
+    // x for the first token group (zero-padded past B) -- overlaps the mask loads
+    {
+        const int nb = min(BT, a.B);
+        const u4* src = reinterpret_cast<const u4*>(a.x);
+        u4* dst = reinterpret_cast<u4*>(s_x);
+        const int n16 = (int)(nb * xrow / 16), all16 = (int)(BT * xrow / 16);
+        for (int k = tid; k < all16; k += FT) dst[k] = k < n16 ? src[k] : u4{0u, 0u, 0u, 0u};
+    }
+    int H, C;
+    if (a.mask) {
+        scan_mask<FT>(a.mask, a.n, s_words, s_scan);
+        const int T = s_scan[words], nhot = a.rows[0];
+        if (nhot >= a.n) {
+            H = T;
+        } else {
+            const int wh = nhot / 64;
+            H = s_scan[wh] + __popcll(s_words[wh] & ((1ull << (nhot % 64)) - 1ull));
+        }
+        C = T - H;
+        if (blockIdx.x == 0 && tid == 0) {
+            a.out_counts[0] = H;
+            a.out_counts[1] = C;
+        }
+    } else {
+        item_counts(a, H, C);
+    }
+    int part, lo, hi, nh;
+    chunk_range(o.nch, H, C, blockIdx.x, part, lo, hi, nh);
+    const int hbase = part == 0 ? 0 : H;              // first item of this partition
+    const uint8_t* wup = part == 0 ? a.up[0] : a.up[1];
+    const uint8_t* wgt = part == 0 ? a.gate[0] : a.gate[1];
+    const uint8_t* wdn = part == 0 ? a.down[0] : a.down[1];
+    const float* bup = part == 0 ? a.bup[0] : a.bup[1];
+    const float* bgt = part == 0 ? a.bgate[0] : a.bgate[1];
+    const int32_t* idx = part == 0 ? a.idx[0] : a.idx[1];
+    const int prows = part == 0 ? a.rows[0] : a.rows[1];
+
+    for (int b0 = 0; b0 < a.B; b0 += BT) {
+        const int nb = min(BT, a.B - b0);
+        if (b0 > 0) {                                  // next token group of x
+            __syncthreads();
+            const u4* src = reinterpret_cast<const u4*>(a.x + b0 * xrow);
+            u4* dst = reinterpret_cast<u4*>(s_x);
+            const int n16 = (int)(nb * xrow / 16), all16 = (int)(BT * xrow / 16);
+            for (int k = tid; k < all16; k += FT) dst[k] = k < n16 ? src[k] : u4{0u, 0u, 0u, 0u};
+        }
+        float acc[BT][NC][EPC];
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[b][k][e] = 0.0f;
+
+        for (int s0 = lo; s0 < hi; s0 += FSTAGE) {
+            const int len = min(FSTAGE, hi - s0);
+            __syncthreads();                           // x staged; previous stage consumed
+            for (int t = tid; t < len; t += FT) {      // resolve this stage's rows
+                const int item = s0 + t;               // position within the partition
+                int row;
+                if (a.mask) {
+                    const int id = kth_active(s_words, s_scan, words, hbase + item);
+                    row = part == 0 ? id : id - a.rows[0];
+                    if (b0 == 0) a.out_idx[part][item] = row;
+                } else {
+                    row = idx ? idx[item] : item;
+                }
+                s_row[t] = (unsigned)row < (unsigned)prows ? row : -1;   // -1: not a row, h = 0
+            }
+            __syncthreads();
+            // groups of G rows, software-pipelined: the loads of the next group are
+            // in flight while the current one is reduced and accumulated; the LDS
+            // reduction slots alternate so each group needs one barrier
+            struct Regs {
+                u4 wu[G][NC], wg[G][NC], wd[G][NC];
+                float su[G][NC], sg[G][NC], sd[G][NC];
+                int row[G];
+            };
+            auto load_group = [&](Regs& R, int g0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int r = s_row[min(g0 + g, len - 1)];
+                    R.row[g] = g0 + g < len ? r : -1;
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int64_t rbase = (int64_t)max(R.row[g], 0) * a.rb;
+#pragma unroll
+                    for (int k = 0; k < NC; ++k) {
+                        const int c = min(tid + FT * k, nch - 1);
+                        R.wu[g][k] = ld16_stream(wup + rbase + 16 * (int64_t)c);
+                        if (ACT == REGLU) R.wg[g][k] = ld16_stream(wgt + rbase + 16 * (int64_t)c);
+                        R.wd[g][k] = ld16_stream(wdn + rbase + 16 * (int64_t)c);
+                    }
+                }
+                if (WT == Q4) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int64_t sbase = (int64_t)max(R.row[g], 0) * a.rb + a.d / 2;
+#pragma unroll
+                        for (int k = 0; k < NC; ++k) {
+                            const int c = min(tid + FT * k, nch - 1);
+                            R.su[g][k] = half_f(*(const uint16_t*)(wup + sbase + 2 * c));
+                            if (ACT == REGLU)
+                                R.sg[g][k] = half_f(*(const uint16_t*)(wgt + sbase + 2 * c));
+                            R.sd[g][k] = half_f(*(const uint16_t*)(wdn + sbase + 2 * c));
+                        }
+                    }
+                }
+            };
+            auto process_group = [&](const Regs& R, int slot) {
+                // partial dot products of this thread's chunks, then wave sums
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) {
+                        float pu = 0.0f, pg = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < NC; ++k) {
+                            const int c = tid + FT * k;
+                            if (c < nch) {
+                                const uint8_t* xp = s_x + b * xrow + (int64_t)c * EPC * XB;
+                                pu = Dot<WT, XT>::run(R.wu[g][k], WT == Q4 ? R.su[g][k] : 0.f, xp, pu);
+                                if (ACT == REGLU)
+                                    pg = Dot<WT, XT>::run(R.wg[g][k], WT == Q4 ? R.sg[g][k] : 0.f, xp,
+                                                          pg);
+                            }
+                        }
+                        pu = wave_sum(pu);
+                        if (ACT == REGLU) pg = wave_sum(pg);
+                        if (lane == 0) {
+                            s_red[slot][wv][g][0][b] = pu;
+                            if (ACT == REGLU) s_red[slot][wv][g][NM - 1][b] = pg;
+                        }
+                    }
+                }
+                __syncthreads();
+                // every thread forms h for the group (same order everywhere), then axpy
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int r = R.row[g];
+                    const float bu = (r >= 0 && bup) ? bup[r] : 0.0f;
+                    const float bg = (ACT == REGLU && r >= 0 && bgt) ? bgt[r] : 0.0f;
+#pragma unroll
+                    for (int b = 0; b < BT; ++b) {
+                        float up = 0.0f, gt = 0.0f;
+#pragma unroll
+                        for (int w = 0; w < FW; ++w) {
+                            up += s_red[slot][w][g][0][b];
+                            if (ACT == REGLU) gt += s_red[slot][w][g][NM - 1][b];
+                        }
+                        up += bu;
+                        float hv;
+                        if (ACT == RELU) {
+                            hv = up > 0.0f ? up : 0.0f;
+                        } else {
+                            gt += bg;
+                            hv = (gt > 0.0f ? gt : 0.0f) * up;
+                        }
+                        if (r < 0 || b >= nb) hv = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < NC; ++k)
+                            Axpy<WT>::run(R.wd[g][k], WT == Q4 ? R.sd[g][k] : 0.f, hv, acc[b][k]);
+                    }
+                }
+            };
+            Regs A, Bn;
+            load_group(A, 0);
+            for (int g0 = 0; g0 < len; g0 += 2 * G) {
+                if (g0 + G < len) load_group(Bn, g0 + G);
+                process_group(A, 0);
+                if (g0 + 2 * G < len) load_group(A, g0 + 2 * G);
+                if (g0 + G < len) process_group(Bn, 1);
+            }
+            __syncthreads();                           // s_red and s_row free for reuse
+        }
+        // this workgroup's partial of y for the token group
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            if (b < nb) {
+                float* prow = o.partials + ((int64_t)blockIdx.x * a.B + b0 + b) * a.d;
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    const int c = tid + FT * k;
+                    if (c < nch) {
+                        f4* dst = reinterpret_cast<f4*>(prow + (int64_t)c * EPC);
+#pragma unroll
+                        for (int e = 0; e < EPC / 4; ++e)
+                            dst[e] = f4{acc[b][k][4 * e], acc[b][k][4 * e + 1], acc[b][k][4 * e + 2],
+                                        acc[b][k][4 * e + 3]};
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Sum of the workgroup partials, fixed order: thread (s, e) adds partials s,
+// s + RS, ... of element e for the hot range and the cold range; the RS slices
+// are then added in slice order.  y_hot, y_cold, y = y_hot + y_cold.
+constexpr int RE = 64;                // output elements per workgroup
+constexpr int RS = 8;                 // partial slices per element
+__global__ __launch_bounds__(RE * RS) void k_reduce_parts(FfnArgs a, DownOut o) {
+    __shared__ float s_h[RS][RE], s_c[RS][RE];
+    const int e = threadIdx.x % RE, s = threadIdx.x / RE;
+    int H, C;
+    if (a.mask) {                      // counts were written by the fused kernel
+        H = a.out_counts[0];
+        C = a.out_counts[1];
+    } else {
+        item_counts(a, H, C);
+    }
+    int part, lo, hi, nh;
+    chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
+    const int64_t len = (int64_t)a.B * a.d;
+    const int64_t at = (int64_t)blockIdx.x * RE + e;
+    const int64_t atc = at < len ? at : len - 1;
+    constexpr int R = 32;
+    float yh = 0.0f, yc = 0.0f;
+    for (int k0 = s; k0 < o.nch; k0 += RS * R) {
+        float v[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) v[q] = o.partials[min(k0 + RS * q, o.nch - 1) * len + atc];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int kk = k0 + RS * q;
+            if (kk < nh) yh += v[q];
+            else if (kk < o.nch) yc += v[q];
+        }
+    }
+    s_h[s][e] = yh;
+    s_c[s][e] = yc;
+    __syncthreads();
+    if (s == 0 && at < len) {
+        float th = 0.0f, tc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < RS; ++q) {
+            th += s_h[q][e];
+            tc += s_c[q][e];
+        }
+        if (o.y_part[0]) o.y_part[0][at] = th;
+        if (o.y_part[1]) o.y_part[1][at] = tc;
+        if (o.y) o.y[at] = th + tc;
+    }
+}
+
+}  // namespace pi

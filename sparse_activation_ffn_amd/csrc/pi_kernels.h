@@ -240,7 +240,78 @@ struct FfnArgs {
     const uint8_t* x;        // [B][d]
     float* h;                // [B][h_ld] per item
     int h_ld;
+    // mask mode (k_up only): the active set comes from mask words over the
+    // n = rows[0] + rows[1] neurons (hot ids < rows[0]); k_up compacts it and
+    // writes the lists and counts that k_down then reads through idx/counts
+    const uint64_t* mask;
+    int n;
+    int32_t* out_idx[2];
+    int32_t* out_counts;
 };
+
+// Largest mask (in 64-bit words) whose compaction k_up does in LDS.
+constexpr int MASK_WORDS_MAX = 4096;
+
+// Position of the j-th set bit (0-based) of v; v has more than j set bits.
+__device__ __forceinline__ int select_bit(uint64_t v, int j) {
+    int pos = 0;
+#pragma unroll
+    for (int w = 32; w > 0; w >>= 1) {
+        const int c = __popcll(v & ((1ull << w) - 1ull));
+        if (j >= c) {
+            j -= c;
+            v >>= w;
+            pos += w;
+        }
+    }
+    return pos;
+}
+
+// Exclusive prefix of the mask words' popcounts into s_scan[0..words] (s_scan[words]
+// = total), with the words copied to s_words; bits at or beyond n are cleared.
+// NT = threads of the calling workgroup.
+template <int NT>
+__device__ void scan_mask(const uint64_t* mask, int n, uint64_t* s_words, int* s_scan) {
+    __shared__ int s_part[NT];
+    const int words = (n + 63) / 64;
+    const int per = (words + NT - 1) / NT;
+    const int w0 = min(words, (int)threadIdx.x * per), w1 = min(words, w0 + per);
+    const uint64_t tail = (n % 64) ? ((1ull << (n % 64)) - 1ull) : ~0ull;
+    int tot = 0;
+    for (int w = w0; w < w1; ++w) {
+        uint64_t v = mask[w];
+        if (w == words - 1) v &= tail;
+        s_words[w] = v;
+        tot += __popcll(v);
+    }
+    s_part[threadIdx.x] = tot;
+    __syncthreads();
+    for (int o = 1; o < NT; o <<= 1) {
+        const int add = (int)threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
+        __syncthreads();
+        s_part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int run = s_part[threadIdx.x] - tot;
+    for (int w = w0; w < w1; ++w) {
+        s_scan[w] = run;
+        run += __popcll(s_words[w]);
+    }
+    if (threadIdx.x == NT - 1) s_scan[words] = s_part[NT - 1];
+    __syncthreads();
+}
+
+// Neuron id of the k-th set bit (ascending) of the scanned mask.
+__device__ __forceinline__ int kth_active(const uint64_t* s_words, const int* s_scan, int words,
+                                          int k) {
+    int lo = 0, hi = words - 1;          // largest w with s_scan[w] <= k
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_scan[mid] <= k) lo = mid;
+        else hi = mid - 1;
+    }
+    return 64 * lo + select_bit(s_words[lo], k - s_scan[lo]);
+}
 
 __device__ __forceinline__ void item_counts(const FfnArgs& a, int& H, int& C) {
     if (a.counts) {
@@ -273,15 +344,38 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
     constexpr int EPC = Chunk<WT>::EPC;
     constexpr int XB = XT == F32 ? 4 : 2;
     constexpr int U = WT == Q4 ? 4 : 8;
-    extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];   // [BT][d] when XLDS
+    // dynamic LDS: [x for BT tokens, when XLDS] [mask words] [their popcount scan]
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+    uint8_t* s_x = s_dyn;
+    const int64_t xrow = (int64_t)a.d * XB;
+    const int words = a.mask ? (a.n + 63) / 64 : 0;
+    uint64_t* s_words = reinterpret_cast<uint64_t*>(s_dyn + (XLDS ? BT * xrow : 0));
+    int* s_scan = reinterpret_cast<int*>(s_words + words);
     const int lane = threadIdx.x & (WAVE - 1);
     const int gw = __builtin_amdgcn_readfirstlane((blockIdx.x * THREADS + threadIdx.x) / WAVE);
     const int nw = gridDim.x * NWAVES;
     int H, C;
-    item_counts(a, H, C);
+    if (a.mask) {
+        // compaction fused here: every workgroup scans the (small) mask in LDS and
+        // maps item k to the k-th active id; hot ids (< rows[0]) come first
+        scan_mask<THREADS>(a.mask, a.n, s_words, s_scan);
+        const int T = s_scan[words], nh = a.rows[0];
+        if (nh >= a.n) {
+            H = T;
+        } else {
+            const int wh = nh / 64;
+            H = s_scan[wh] + __popcll(s_words[wh] & ((1ull << (nh % 64)) - 1ull));
+        }
+        C = T - H;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.out_counts[0] = H;
+            a.out_counts[1] = C;
+        }
+    } else {
+        item_counts(a, H, C);
+    }
     const int T = H + C;
     const int nch = a.d / EPC;
-    const int64_t xrow = (int64_t)a.d * XB;
     for (int b0 = 0; b0 < a.B; b0 += BT) {
         const int nb = min(BT, a.B - b0);
         if (XLDS) {
@@ -296,7 +390,14 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
         const uint8_t* xg = XLDS ? s_x : a.x + b0 * xrow;
         for (int item = gw; item < T; item += nw) {
             int part, row;
-            item_row(a, item, H, part, row);
+            if (a.mask) {
+                const int id = kth_active(s_words, s_scan, words, item);
+                part = id < a.rows[0] ? 0 : 1;
+                row = part == 0 ? id : id - a.rows[0];
+                if (lane == 0 && b0 == 0) a.out_idx[part][part == 0 ? item : item - H] = row;
+            } else {
+                item_row(a, item, H, part, row);
+            }
             if ((unsigned)row >= (unsigned)a.rows[part]) {     // id outside the partition: h = 0
                 if (lane == 0)
                     for (int b = 0; b < nb; ++b) a.h[(int64_t)(b0 + b) * a.h_ld + item] = 0.0f;
@@ -490,10 +591,20 @@ __global__ __launch_bounds__(THREADS) void k_reduce(FfnArgs a, DownOut o) {
     chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
     const int64_t len = (int64_t)a.B * a.d;
     const int64_t stride = (int64_t)gridDim.x * THREADS;
+    constexpr int R = 32;      // partial loads in flight per thread (branch-free batches)
     for (int64_t at = (int64_t)blockIdx.x * THREADS + threadIdx.x; at < len; at += stride) {
         float yh = 0.0f, yc = 0.0f;
-        for (int kk = 0; kk < nh; ++kk) yh += o.partials[kk * len + at];
-        for (int kk = nh; kk < o.nch; ++kk) yc += o.partials[kk * len + at];
+        for (int k0 = 0; k0 < o.nch; k0 += R) {
+            float v[R];
+#pragma unroll
+            for (int q = 0; q < R; ++q) v[q] = o.partials[min(k0 + q, o.nch - 1) * len + at];
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int kk = k0 + q;
+                if (kk < nh) yh += v[q];
+                else if (kk < o.nch) yc += v[q];
+            }
+        }
         if (o.y_part[0]) o.y_part[0][at] = yh;
         if (o.y_part[1]) o.y_part[1][at] = yc;
         if (o.y) o.y[at] = yh + yc;

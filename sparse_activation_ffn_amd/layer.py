@@ -115,11 +115,13 @@ class StepBuffers:
 
 
 def decode_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, pred=None, parts=None,
-                partials: bool = False, stream=None):
-    """predict (+fused compaction) -> sparse FFN on hot and cold -> merge, on one stream."""
+                partials: bool = False, logits=None, stream=None):
+    """predict -> (compaction fused into) sparse FFN on hot and cold -> merge, on one stream.
+    buf.lists receives the active lists as a side output."""
     pred = layer.predictor() if pred is None else pred
     hot, cold = layer.parts() if parts is None else parts
-    pb.pi_predict(pred, x, buf.mask, None, buf.lists, buf.ws, stream)
+    pb.pi_predict(pred, x, buf.mask, logits, None, buf.ws, stream)
     pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, buf.y_hot if partials else None,
-                           buf.y_cold if partials else None, buf.y, buf.ws, stream)
+                           buf.y_cold if partials and cold is not None else None, buf.y, buf.ws,
+                           stream, mask=buf.mask)
     return buf.y

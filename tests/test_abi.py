@@ -104,14 +104,18 @@ def test_sparse_ffn_validation(L):
 def test_split_validation(L):
     hot, cold = _part(rows=30), _part(rows=70, d=512)
     lists = pb.ActiveLists(30, FAKE, FAKE, FAKE)
-    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, C.byref(lists),
-                               None, None, FAKE, FAKE, 1 << 24, None)
+    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, None,
+                               C.byref(lists), None, None, FAKE, FAKE, 1 << 24, None)
     assert rc == pb.PI_ERR_SHAPE          # hot and cold differ in d
     lists.n_hot = 31
     cold = _part(rows=70)
-    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, C.byref(lists),
-                               None, None, FAKE, FAKE, 1 << 24, None)
+    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, None,
+                               C.byref(lists), None, None, FAKE, FAKE, 1 << 24, None)
     assert rc == pb.PI_ERR_SHAPE          # n_hot != hot rows
+    lists.n_hot = 30
+    rc = L.pi_sparse_ffn_split(C.byref(hot), C.byref(cold), FAKE, 1, pb.PI_F16, FAKE + 4,
+                               C.byref(lists), None, None, FAKE, FAKE, 1 << 24, None)
+    assert rc == pb.PI_ERR_ALIGN          # mask misaligned
 
 
 def test_compact_merge_copy_validation(L):

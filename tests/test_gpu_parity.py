@@ -30,14 +30,21 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def run_step(dl: DeviceLayer, buf: StepBuffers, x_np, logits=True, partials=True):
+def run_step(dl: DeviceLayer, buf: StepBuffers, x_np, logits=True, partials=True, fused=True):
+    """One decode step through the C ABI.  fused: pi_predict writes the mask and
+    pi_sparse_ffn_split compacts it (lists as side output); otherwise pi_predict
+    compacts into lists and pi_sparse_ffn_split reads them."""
     x = torch.from_numpy(x_np).to(DEV)
     B = x_np.shape[0]
     lg = torch.empty((B, dl.n), dtype=torch.float32, device=DEV) if logits else None
     hot, cold = dl.parts()
-    pb.pi_predict(dl.predictor(), x, buf.mask, lg, buf.lists, buf.ws)
+    buf.hot_idx.fill_(-7)
+    buf.cold_idx.fill_(-7)
+    buf.counts.fill_(-7)
+    pb.pi_predict(dl.predictor(), x, buf.mask, lg, None if fused else buf.lists, buf.ws)
     pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, buf.y_hot if partials else None,
-                           buf.y_cold if partials and cold is not None else None, buf.y, buf.ws)
+                           buf.y_cold if partials and cold is not None else None, buf.y, buf.ws,
+                           mask=buf.mask if fused else None)
     torch.cuda.synchronize()
     c = _np(buf.counts)
     out = dict(mask=_np(buf.mask).view(np.uint64), counts=c, hot=_np(buf.hot_idx)[:c[0]],
@@ -131,7 +138,7 @@ def test_small_parity(name, B):
     buf = StepBuffers(dl, B, DEV)
     for step in range(4):
         x = S.make_x(wl, 0, step, B)
-        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x))
+        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step % 2 == 0)))
         log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
 
 
@@ -144,7 +151,7 @@ def test_fp32_layer_all_decode_tokens():
     worst = 0.0
     for step in range(wl.steps):
         x = S.make_x(wl, 0, step, 1)
-        e, _, _ = check_step(L, wl.n, x, run_step(dl, buf, x))
+        e, _, _ = check_step(L, wl.n, x, run_step(dl, buf, x, fused=(step % 2 == 0)))
         worst = max(worst, e)
     log(f"  fp32 full: worst normwise max-rel error {worst:.2e} over {wl.steps} tokens")
 
@@ -186,7 +193,7 @@ def test_split_points(small_f16, n_hot):
     buf = StepBuffers(dl, 1, DEV)
     for step in range(2):
         x = S.make_x(wl, 0, step, 1)
-        check_step(L, n_hot, x, run_step(dl, buf, x))
+        check_step(L, n_hot, x, run_step(dl, buf, x, fused=(step == 0)))
 
 
 def test_deterministic_reruns(small_f16):
