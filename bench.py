@@ -77,6 +77,25 @@ def step_bytes(wl, B, active):
     return pred + active * (m * wrow_bytes(wl) + 4) + B * wl.d * esize(wl.xdtype) + 4 * B * wl.d
 
 
+def counter_traffic(wl_name, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter record
+    (profiles/<workload>_traffic.json: FETCH_SIZE and WRITE_SIZE passes scaled by a
+    plain copy of known size), or None when there is no record or the kernel sources
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{wl_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("pi_device.h", "pi_kernels.h", "pi_ffn.h", "pi_api.hip"):
+        h.update(open(os.path.join(ROOT, "sparse_activation_ffn_amd", "csrc", f), "rb").read())
+    k = rec.get("kernels", {}).get(kernel)
+    if rec.get("source_sha256") != h.hexdigest() or k is None:
+        return None
+    return k["read_bytes"] + k["write_bytes"]
+
+
 def cpu_baseline(wl, L, n_hot, B, budget_s=12.0):
     """The oracle's layer step (predict, compact, sparse FFN per partition, merge) on the host."""
     from oracle import oracle as O
@@ -204,7 +223,8 @@ def main():
     dom_gbps = kb_mean[dom] / (kern_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": None}
+                "algorithmic_bytes": round(kb_mean[dom]),
+                "traffic": counter_traffic(wl.name, dom)}
 
     dense = None
     if not args.no_dense:
