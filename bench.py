@@ -116,6 +116,110 @@ def cpu_baseline(wl, L, n_hot, B, budget_s=12.0):
                       f"single-threaded C oracle, fp64 accumulation"}
 
 
+def stack_main(args, wl):
+    """The Falcon-40B-shaped FFN stack: 60 distinct layers, each with its own
+    predictor and a 20% hot partition indexed from 1024 profiling samples; a decode
+    step runs all 60 layer steps (fresh x per step and layer).  Layers are drawn on
+    the GPU (workload.synth.make_layer_device).  Reports µs per layer step and
+    tokens/s of the FFN stack."""
+    import torch
+    from sparse_activation_ffn_amd import binding as pb
+    from sparse_activation_ffn_amd.layer import DeviceLayer, StepBuffers
+    from workload import synth as S
+    dev = "cuda:0"
+    B, K, W = args.batch, args.steps, args.warmup
+    NL = wl.layers
+    layers = []
+    log(f"[bench] drawing, profiling and indexing {NL} layers on the GPU ...")
+    for li in range(NL):
+        ly = DeviceLayer.from_tensors(wl, S.make_layer_device(wl, li, dev))
+        g = torch.Generator(device=dev)
+        g.manual_seed(S.SEED + 7 * li + 1)
+        X = torch.randn(wl.profile_samples, wl.d, generator=g, device=dev).to(torch.float16)
+        counts = ly.profile_counts(X)
+        perm, n_hot = ly.build_index(counts, S.budget_bytes(wl), S.bytes_per_neuron(wl))
+        ly.apply_index(perm, n_hot)
+        layers.append(ly)
+        del X
+    torch.cuda.synchronize()
+    descs = [(ly.predictor(), ly.parts()) for ly in layers]
+    buf = StepBuffers(layers[0], B, dev)
+    gx = torch.Generator(device=dev)
+    gx.manual_seed(S.SEED + 99)
+    xs = torch.randn(W + K, NL, B, wl.d, generator=gx, device=dev).to(torch.float16)
+
+    def layer_step(s, li):
+        pred, (hot, cold) = descs[li]
+        x = xs[s, li]
+        pb.pi_predict(pred, x, buf.mask, None, None, buf.ws)
+        pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, None, None, buf.y, buf.ws, mask=buf.mask)
+
+    log(f"[bench] warmup {W} + timed {K} decode steps x {NL} layers ...")
+    for s in range(W):
+        for li in range(NL):
+            layer_step(s, li)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(W, W + K):
+            for li in range(NL):
+                layer_step(s, li)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_layer = e0.elapsed_time(e1) * 1e3 / (K * NL)
+    # per-kernel durations and active counts over the first timed step
+    kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2, "k_ffn": pb.PI_K_FFN,
+            "k_reduce": pb.PI_K_REDUCE}
+    for kid in kids.values():
+        pb.pi_kernel_timer_start(kid, NL)
+    active = []
+    for li in range(NL):
+        layer_step(W, li)
+        active.append(int(buf.counts.sum().item()))
+    kern = {name: pb.pi_kernel_timer_stop(kid) for name, kid in kids.items()}
+    kern_us = {k: ms * 1e3 / max(n, 1) for k, (ms, n) in kern.items() if n}
+    kb = [kernel_bytes(wl, B, a) for a in active]
+    kb_mean = {k: float(np.mean([b[k] for b in kb])) for k in kern_us}
+    dom = max(kern_us, key=kern_us.get)
+    dom_gbps = kb_mean[dom] / (kern_us[dom] * 1e-6) / 1e9
+    touched = float(np.mean([step_bytes(wl, B, a) for a in active]))
+    gbps = touched / (us_layer * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (host-drawn layer 59) ...")
+        L = S.make_layer(wl, layer=NL - 1)
+        cpu = cpu_baseline(wl, L, int(wl.hot_frac * wl.n), B)
+        cpu["sample"] += " (layer 59 unpermuted, first 20% of rows as the hot partition)"
+    out = {
+        "metric": METRIC, "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(us_layer * NL / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": NL, "d_model": wl.d, "d_ffn": wl.n,
+                   "predictor_rank": wl.r, "batch": B, "weights": wl.wdtype,
+                   "accumulate": "f32", "hot_fraction": wl.hot_frac,
+                   "mean_active": round(float(np.mean(active)), 1)},
+        "timing": "hip_graph",
+        "tokens_per_s_ffn_stack": round(1e6 / (us_layer * NL), 1),
+        "touched_bytes_per_layer_step": round(touched),
+        "achieved_gbps_touched": round(gbps, 1),
+        "frac_of_peak_touched": round(gbps / PEAK_HBM_GBPS, 4),
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
+                     "algorithmic_bytes": round(kb_mean[dom]),
+                     "traffic": counter_traffic(wl.name, dom)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +246,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = S.WORKLOADS[args.workload]
+    if wl.layers > 1:
+        return stack_main(args, wl)
     B = args.batch
     K, W = args.steps, args.warmup
     log(f"[bench] generating {wl.name} layer ...")

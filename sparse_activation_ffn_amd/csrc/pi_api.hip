@@ -55,7 +55,10 @@ int pick_nch(int d, int wt, int B) {
 }
 
 // Fused kernel (k_ffn): one workgroup per compute unit of the MI355X.
-constexpr int NWG_FUSED = 256;
+#ifndef PI_FFN_WORKGROUPS
+#define PI_FFN_WORKGROUPS 256
+#endif
+constexpr int NWG_FUSED = PI_FFN_WORKGROUPS;
 constexpr int FUSED_MAX_BATCH = 4;
 
 // 16-byte chunks per thread of k_ffn for rows of d elements (1, 2 or 4; 0 = too wide)

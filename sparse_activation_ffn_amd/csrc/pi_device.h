@@ -19,8 +19,16 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// Weight streams are read once per step: non-temporal loads by default.
+#ifndef PI_WEIGHT_NT
+#define PI_WEIGHT_NT 1
+#endif
 __device__ __forceinline__ u4 ld16_stream(const void* p) {
+#if PI_WEIGHT_NT
     return __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+#else
+    return *reinterpret_cast<const u4*>(p);
+#endif
 }
 __device__ __forceinline__ u4 ld16(const void* p) { return *reinterpret_cast<const u4*>(p); }
 __device__ __forceinline__ u2 ld8_stream(const void* p) {

@@ -18,7 +18,10 @@
 
 namespace pi {
 
-constexpr int FT = 512;               // threads of the fused kernel (8 waves)
+#ifndef PI_FFN_THREADS
+#define PI_FFN_THREADS 512
+#endif
+constexpr int FT = PI_FFN_THREADS;    // threads of the fused kernel (8 waves)
 constexpr int FW = FT / WAVE;
 constexpr int FSTAGE = 256;           // item rows resolved into LDS at a time
 

@@ -284,20 +284,32 @@ __device__ void scan_mask(const uint64_t* mask, int n, uint64_t* s_words, int* s
         s_words[w] = v;
         tot += __popcll(v);
     }
-    s_part[threadIdx.x] = tot;
-    __syncthreads();
-    for (int o = 1; o < NT; o <<= 1) {
-        const int add = (int)threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
-        __syncthreads();
-        s_part[threadIdx.x] += add;
-        __syncthreads();
+    // inclusive scan of the per-thread totals: within each wave by shuffles, then
+    // across the NT / 64 wave totals
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    int inc = tot;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int v = __shfl_up(inc, o, WAVE);
+        if (lane >= o) inc += v;
     }
-    int run = s_part[threadIdx.x] - tot;
+    if (lane == WAVE - 1) s_part[wv] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int k = 0; k < NT / WAVE; ++k) {
+            const int t = s_part[k];
+            s_part[k] = acc;                 // exclusive prefix of the wave totals
+            acc += t;
+        }
+        s_scan[words] = acc;
+    }
+    __syncthreads();
+    int run = s_part[wv] + inc - tot;
     for (int w = w0; w < w1; ++w) {
         s_scan[w] = run;
         run += __popcll(s_words[w]);
     }
-    if (threadIdx.x == NT - 1) s_scan[words] = s_part[NT - 1];
     __syncthreads();
 }
 

@@ -45,6 +45,13 @@ class DeviceLayer:
                    _dev(L.b_gate, device), _dev(L.P1t, device), _dev(L.P2t, device),
                    _dev(L.b2, device), L.threshold, n_hot)
 
+    @classmethod
+    def from_tensors(cls, wl, t: dict, n_hot=None):
+        """From device tensors with the Layer field names (workload.synth.make_layer_device)."""
+        return cls(wl.d, wl.n, wl.r, wl.act, wl.wdtype == "q4_0", t["W_up"], t["W_gate"],
+                   t["W_downT"], t["b_up"], t["b_gate"], t["P1t"], t["P2t"], t["b2"],
+                   t["threshold"], n_hot)
+
     def clone(self):
         """Same values at new device addresses (another instance of the layer)."""
         c = lambda t: None if t is None else t.clone()  # noqa: E731

@@ -297,3 +297,41 @@ def budget_bytes(wl: Workload) -> int:
     if wl.hot_frac is None:
         return wl.n * bytes_per_neuron(wl)
     return int(wl.hot_frac * wl.n * bytes_per_neuron(wl))
+
+
+def make_layer_device(wl: Workload, layer: int, device="cuda"):
+    """The same recipe drawn on the GPU with torch's generator (seeded per workload and
+    layer), for timing runs over many layers where host generation would take minutes.
+    Float workloads only.  Values differ from make_layer's (different generator); the
+    shapes, distributions, biases and firing rates are the same.  Returns a dict of
+    device tensors with the Layer field names."""
+    import torch
+    if wl.wdtype == Q4_0:
+        raise ValueError("device generation covers f32/f16 workloads")
+    d, n, r = wl.d, wl.n, wl.r
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED * 1000003 + wl.key * 1009 + layer)
+    dt = torch.float16 if wl.wdtype == F16 else torch.float32
+    pdt = torch.float16 if wl.pdtype == F16 else torch.float32
+    z = torch.from_numpy(ndtri(neuron_probs(wl, layer))).to(device)
+
+    def normal(rows, cols, std, dtype):
+        out = torch.empty(rows, cols, dtype=dtype, device=device)
+        for r0 in range(0, rows, 4096):
+            blk = torch.randn(min(4096, rows - r0), cols, generator=g, device=device)
+            out[r0:r0 + blk.shape[0]] = (blk * std).to(dtype)
+        return out
+
+    W_up = normal(n, d, 1.0 / math.sqrt(d), dt)
+    W_downT = normal(n, d, 1.0 / math.sqrt(n), dt)
+    W_gate = b_up = b_gate = None
+    if wl.act == REGLU:
+        W_gate = normal(n, d, 1.0 / math.sqrt(d), dt)
+        b_gate = (W_gate.float().norm(dim=1).double() * z).float()
+    else:
+        b_up = (W_up.float().norm(dim=1).double() * z).float()
+    P1t = normal(r, d, 1.0 / math.sqrt(d), pdt)
+    P2t = normal(n, r, 1.0 / math.sqrt(r), pdt)
+    b2 = (z / math.sqrt(2.0)).float()
+    return dict(W_up=W_up, W_gate=W_gate, W_downT=W_downT, b_up=b_up, b_gate=b_gate, P1t=P1t,
+                P2t=P2t, b2=b2, threshold=0.0)
