@@ -12,6 +12,7 @@
 #include "pi.h"
 #include "pi_ffn.h"
 #include "pi_kernels.h"
+#include "pi_mfma.h"
 
 using namespace pi;
 
@@ -79,6 +80,18 @@ bool use_fused(int d, int wt, int xt, int B) {
     if (wt == Q4 && (B > 1 || nc == 4)) return false;
     if (nc == 4 && B > 1) return false;
     return true;
+}
+
+// Matrix-core path: batches of 16..64 tokens with f16 x and f16 / Q4_0 weights.
+constexpr int MFMA_MIN_BATCH = 16;
+bool use_mfma(int d, int wt, int xt, int B) {
+    return B >= MFMA_MIN_BATCH && B <= MM && xt == F16 && (wt == F16 || wt == Q4) && d % DC == 0;
+}
+// split-K chunks of the MFMA down kernel: about 512 workgroups in total
+int mfma_chunks(int d) {
+    const int tiles = d / DC;
+    const int k = 512 / (tiles > 0 ? tiles : 1);
+    return k < 2 ? 2 : k > NCH_MAX ? NCH_MAX : k;
 }
 
 size_t ws_pred_bytes(int r, int B) { return WS_CTR_BYTES + align256((size_t)B * r * 4); }
@@ -289,6 +302,22 @@ pi_status run_fused(const FfnArgs& a, const DownOut& o, int wt, int act, hipStre
     return fused_act<Q4, F16, 1>(a, o, act, s);          // Q4_0: batch 1 only (use_fused)
 }
 
+// ---- matrix-core path -------------------------------------------------------
+template <int WT>
+pi_status run_mfma_wt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
+    _Float16* h16 = reinterpret_cast<_Float16*>(a.h);
+    const int ugrid = (rows_cap + UR - 1) / UR > 0 ? (rows_cap + UR - 1) / UR : 1;
+    if (act == PI_RELU)
+        TRY(launch(PI_K_UP, k_mfma_up<WT, RELU>, dim3(ugrid), dim3(256), 0, s, a, h16));
+    else
+        TRY(launch(PI_K_UP, k_mfma_up<WT, REGLU>, dim3(ugrid), dim3(256), 0, s, a, h16));
+    TRY(launch(PI_K_DOWN, k_mfma_down<WT>, dim3(a.d / DC, o.nch), dim3(256), 0, s, a, o,
+               (const _Float16*)h16));
+    const int64_t len = (int64_t)a.B * a.d;
+    return launch(PI_K_REDUCE, k_reduce_parts, dim3((unsigned)((len + RE - 1) / RE)),
+                  dim3(RE * RS), 0, s, a, o);
+}
+
 pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, int rows_cap,
                   hipStream_t s) {
     if (wt == F32) return xt == F32 ? ffn_bt<F32, F32>(a, o, act, rows_cap, s) : ffn_bt<F32, F16>(a, o, act, rows_cap, s);
@@ -323,7 +352,8 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     const int d = hot->d, wt = hot->wdtype;
     const int n = hot->rows + (has_cold ? cold->rows : 0);
     const bool fused = use_fused(d, wt, xdtype, B);
-    const int nch = fused ? NWG_FUSED : pick_nch(d, wt, B);
+    const bool mfma = !fused && use_mfma(d, wt, xdtype, B);
+    const int nch = fused ? NWG_FUSED : mfma ? mfma_chunks(d) : pick_nch(d, wt, B);
     TRY(check_ws(ws, ws_bytes, ws_ffn_bytes(d, n, B, nch)));
 
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -350,8 +380,8 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
         CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
         Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),
                 const_cast<int32_t*>(counts)};
-        if ((n + 63) / 64 <= MASK_WORDS_MAX) {
-            a.mask = mask;                   // compaction fused into k_up
+        if (!mfma && (n + 63) / 64 <= MASK_WORDS_MAX) {
+            a.mask = mask;                   // compaction fused into k_ffn / k_up
             a.n = n;
             a.out_idx[0] = L.hot;
             a.out_idx[1] = L.cold;
@@ -374,6 +404,8 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     o.y = y;
     o.nch = nch;
     if (fused) return run_fused(a, o, wt, hot->act, s);
+    if (mfma)
+        return wt == F16 ? run_mfma_wt<F16>(a, o, hot->act, n, s) : run_mfma_wt<Q4>(a, o, hot->act, n, s);
     return run_ffn(a, o, wt, xdtype, hot->act, n, s);
 }
 
@@ -415,6 +447,10 @@ size_t pi_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t B) {
         if (f > need) need = f;
         if (B <= FUSED_MAX_BATCH) {
             f = ws_ffn_bytes(d, n, B, NWG_FUSED);
+            if (f > need) need = f;
+        }
+        if (B >= MFMA_MIN_BATCH) {
+            f = ws_ffn_bytes(d, n, B, mfma_chunks(d));
             if (f > need) need = f;
         }
     }

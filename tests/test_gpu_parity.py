@@ -142,6 +142,33 @@ def test_small_parity(name, B):
         log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
 
 
+MFMA_SMALL = {
+    "reglu-f16": S.WORKLOADS["llama70b-reglu-fp16"].scaled(d=768, n=1333, r=64),
+    "relu-f16-split": S.WORKLOADS["opt30b-fp16"].scaled(d=512, n=1500, r=32),
+    "q4_0": S.WORKLOADS["opt175b-q4_0"].scaled(d=1280, n=1111, r=64),
+}
+
+
+@pytest.mark.parametrize("name,B", [("reglu-f16", 16), ("reglu-f16", 33), ("relu-f16-split", 64),
+                                    ("q4_0", 20), ("q4_0", 64)])
+def test_matrix_core_batches(name, B):
+    """Batches of 16..64 tokens (matrix-core path): union active set, f16-rounded h and
+    dequantised weights, checked to the fp16 / Q4_0 tolerance."""
+    wl = MFMA_SMALL[name]
+    log(f"matrix-core {name} B={B}")
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    if wl.hot_frac is not None:
+        Lh, n_hot = index_layer(L, dl, 256)
+    else:
+        Lh, n_hot = L, wl.n
+    buf = StepBuffers(dl, B, DEV)
+    for step in range(2):
+        x = S.make_x(wl, 0, step, B)
+        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step == 0)))
+        log(f"  step {step}: union active {na}, ambiguous {namb}, err {e:.2e}")
+
+
 def test_fp32_layer_all_decode_tokens():
     """OPT-style fp32 layer at full size (d 1024, n 4096, rank 128), all 64 decode tokens."""
     wl = S.WORKLOADS["opt-fp32"]
