@@ -167,6 +167,16 @@ pi_status check_ws(void* ws, size_t have, size_t need) {
     } while (0)
 
 // ---- template dispatch ---------------------------------------------------------
+// kernels with more than 64 KiB of dynamic LDS must opt in
+template <typename K>
+pi_status allow_lds(K kernel, size_t bytes) {
+    if (bytes <= 65536) return PI_OK;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return fail(PI_ERR_HIP, "LDS attribute: %s", hipGetErrorString(e));
+    return PI_OK;
+}
+
 template <int WT, int XT, int BT>
 pi_status launch_pred_l1(const pi_predictor* p, const void* x, int B, float* u, hipStream_t s) {
     return launch(PI_K_PRED_L1, k_pred_l1<WT, XT, BT>, dim3(p->r), dim3(THREADS), 0, s,
@@ -186,10 +196,13 @@ pi_status pred_l1_bt(const pi_predictor* p, const void* x, int B, float* u, hipS
 template <int WT, int BT>
 pi_status launch_pred_l2(const pi_predictor* p, const float* u, int B, uint64_t* mask, float* logits,
                          hipStream_t s) {
-    const int grid = (p->n + 63) / 64;
-    return launch(PI_K_PRED_L2, k_pred_l2<WT, BT>, dim3(grid), dim3(THREADS),
-                  (size_t)BT * p->r * sizeof(float), s, (const uint8_t*)p->P2t, p->b2,
-                  p->threshold, u, p->n, p->r, B, mask, logits);
+    // one workgroup per 16-bit quarter of every mask word (tail quarters included)
+    const int grid = (p->n + 63) / 64 * (64 / L2_ROWS);
+    const size_t sh = (size_t)BT * p->r * sizeof(float);
+    auto kern = k_pred_l2<WT, BT>;
+    TRY(allow_lds(kern, sh));
+    return launch(PI_K_PRED_L2, kern, dim3(grid), dim3(THREADS), sh, s, (const uint8_t*)p->P2t,
+                  p->b2, p->threshold, u, p->n, p->r, B, reinterpret_cast<uint16_t*>(mask), logits);
 }
 
 template <int WT>
@@ -250,20 +263,12 @@ pi_status ffn_bt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipS
 }
 
 // ---- fused path -------------------------------------------------------------
-template <typename K>
-pi_status allow_lds(K kernel, size_t bytes) {
-    if (bytes <= 65536) return PI_OK;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return fail(PI_ERR_HIP, "LDS attribute: %s", hipGetErrorString(e));
-    return PI_OK;
-}
 
 template <int WT, int XT, int BT, int ACT, int NC>
 pi_status launch_fused(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
     const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
-    const size_t sh = xbytes + (words ? words * 8 + (words + 1) * 4 : 0);
+    const size_t sh = xbytes + words * 8;            // x, then the mask words
     auto kern = k_ffn<WT, XT, BT, ACT, NC>;
     TRY(allow_lds(kern, sh));
     TRY(launch(PI_K_FFN, kern, dim3(o.nch), dim3(FT), sh, s, a, o));

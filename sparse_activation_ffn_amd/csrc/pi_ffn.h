@@ -71,21 +71,32 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     constexpr int G0 = (WT == Q4 ? 4 : 8) / NC / (ACT == REGLU ? 2 : 1) / (BT >= 4 ? 2 : 1);
     constexpr int G = G0 > 0 ? G0 : 1;
     constexpr int NM = ACT == REGLU ? 2 : 1;          // dot products per row (up, gate)
-    // dynamic LDS: [x for BT tokens] [mask words] [their popcount scan]
+    // dynamic LDS: [x for BT tokens] [mask words]
     extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ int s_row[FSTAGE];
     __shared__ float s_red[2][FW][G][NM][BT];
+    __shared__ int s_wtot[FW];
+    __shared__ int s_hot;
     const int64_t xrow = (int64_t)a.d * XB;
     uint8_t* s_x = s_dyn;
-    const int words = a.mask ? (a.n + 63) / 64 : 0;
     uint64_t* s_words = reinterpret_cast<uint64_t*>(s_dyn + BT * xrow);
-    int* s_scan = reinterpret_cast<int*>(s_words + words);
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
     const int wv = tid / WAVE;
     const int nch = a.d / EPC;                         // 16-byte (code) chunks of a row
 
-    // x for the first token group (zero-padded past B) -- overlaps the mask loads
+    // Prologue, one memory round trip: this thread's run of mask words and its
+    // share of x are loaded together, before anything waits on either.
+    constexpr int PMAX = (MASK_WORDS_MAX + FT - 1) / FT;
+    const int words = a.mask ? (a.n + 63) / 64 : 0;
+    const int per = (words + FT - 1) / FT;             // mask words per thread (<= PMAX)
+    const int w0 = tid * per;
+    uint64_t mw[PMAX];
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q) {
+        mw[q] = 0;
+        if (q < per && w0 + q < words) mw[q] = a.mask[w0 + q];
+    }
     {
         const int nb = min(BT, a.B);
         const u4* src = reinterpret_cast<const u4*>(a.x);
@@ -94,14 +105,54 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
         for (int k = tid; k < all16; k += FT) dst[k] = k < n16 ? src[k] : u4{0u, 0u, 0u, 0u};
     }
     int H, C;
+    int run = 0;                                       // rank of this thread's first set bit
     if (a.mask) {
-        scan_mask<FT>(a.mask, a.n, s_words, s_scan);
-        const int T = s_scan[words], nhot = a.rows[0];
+        if (a.n % 64) {                                // bits past n are not neurons
+#pragma unroll
+            for (int q = 0; q < PMAX; ++q)
+                if (q < per && w0 + q == words - 1) mw[q] &= (1ull << (a.n % 64)) - 1ull;
+        }
+        int tot = 0;
+#pragma unroll
+        for (int q = 0; q < PMAX; ++q) {
+            tot += __popcll(mw[q]);
+            if (q < per && w0 + q < words) s_words[w0 + q] = mw[q];   // for the row emission
+        }
+        // exclusive scan of the per-thread totals: shuffles in the wave, then the
+        // FW wave totals through LDS
+        int inc = tot;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const int v = __shfl_up(inc, o, WAVE);
+            if (lane >= o) inc += v;
+        }
+        if (lane == WAVE - 1) s_wtot[wv] = inc;
+        // the thread holding bit nhot of the mask finds H (hot ranks are [0, H))
+        const int nhot = a.rows[0];
+        __syncthreads();
+        int before = 0, T = 0;
+#pragma unroll
+        for (int w = 0; w < FW; ++w) {
+            const int t = s_wtot[w];
+            before += w < wv ? t : 0;
+            T += t;
+        }
+        run = before + inc - tot;
         if (nhot >= a.n) {
             H = T;
         } else {
             const int wh = nhot / 64;
-            H = s_scan[wh] + __popcll(s_words[wh] & ((1ull << (nhot % 64)) - 1ull));
+            if (wh >= w0 && wh < w0 + per) {
+                int h = run;
+#pragma unroll
+                for (int q = 0; q < PMAX; ++q) {
+                    if (w0 + q < wh) h += __popcll(mw[q]);
+                    else if (w0 + q == wh) h += __popcll(mw[q] & ((1ull << (nhot % 64)) - 1ull));
+                }
+                s_hot = h;
+            }
+            __syncthreads();
+            H = s_hot;
         }
         C = T - H;
         if (blockIdx.x == 0 && tid == 0) {
@@ -142,17 +193,34 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
         for (int s0 = lo; s0 < hi; s0 += FSTAGE) {
             const int len = min(FSTAGE, hi - s0);
             __syncthreads();                           // x staged; previous stage consumed
-            for (int t = tid; t < len; t += FT) {      // resolve this stage's rows
-                const int item = s0 + t;               // position within the partition
-                int row;
-                if (a.mask) {
-                    const int id = kth_active(s_words, s_scan, words, hbase + item);
-                    row = part == 0 ? id : id - a.rows[0];
-                    if (b0 == 0) a.out_idx[part][item] = row;
-                } else {
-                    row = idx ? idx[item] : item;
+            if (a.mask) {
+                // each thread emits the set bits of its words whose ranks fall in
+                // this stage's item range [gb, ge) (all in this partition)
+                const int gb = hbase + s0, ge = gb + len;
+                int r0 = run;
+#pragma unroll
+                for (int q = 0; q < PMAX; ++q) {
+                    if (q >= per || w0 + q >= words) break;
+                    uint64_t v = s_words[w0 + q];
+                    const int pc = __popcll(v);
+                    if (pc > 0 && r0 < ge && r0 + pc > gb) {
+                        const int skip = max(0, gb - r0);
+                        if (skip > 0) v &= ~((1ull << select_bit(v, skip)) - 1ull);
+                        for (int rank = r0 + skip; v != 0 && rank < ge; ++rank) {
+                            const int id = 64 * (w0 + q) + __builtin_ctzll(v);
+                            v &= v - 1ull;
+                            const int row = part == 0 ? id : id - a.rows[0];
+                            s_row[rank - gb] = (unsigned)row < (unsigned)prows ? row : -1;
+                            if (b0 == 0) a.out_idx[part][rank - hbase] = row;
+                        }
+                    }
+                    r0 += pc;
                 }
-                s_row[t] = (unsigned)row < (unsigned)prows ? row : -1;   // -1: not a row, h = 0
+            } else {
+                for (int t = tid; t < len; t += FT) {  // resolve this stage's rows
+                    const int row = idx ? idx[s0 + t] : s0 + t;
+                    s_row[t] = (unsigned)row < (unsigned)prows ? row : -1;   // -1: not a row, h = 0
+                }
             }
             __syncthreads();
             // groups of G rows, software-pipelined: the loads of the next group are
@@ -285,8 +353,8 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
 // Sum of the workgroup partials, fixed order: thread (s, e) adds partials s,
 // s + RS, ... of element e for the hot range and the cold range; the RS slices
 // are then added in slice order.  y_hot, y_cold, y = y_hot + y_cold.
-constexpr int RE = 64;                // output elements per workgroup
-constexpr int RS = 8;                 // partial slices per element
+constexpr int RE = 32;                // output elements per workgroup (one 128-byte line)
+constexpr int RS = 16;                // partial slices per element
 __global__ __launch_bounds__(RE * RS) void k_reduce_parts(FfnArgs a, DownOut o) {
     __shared__ float s_h[RS][RE], s_c[RS][RE];
     const int e = threadIdx.x % RE, s = threadIdx.x / RE;
@@ -302,7 +370,7 @@ __global__ __launch_bounds__(RE * RS) void k_reduce_parts(FfnArgs a, DownOut o) 
     const int64_t len = (int64_t)a.B * a.d;
     const int64_t at = (int64_t)blockIdx.x * RE + e;
     const int64_t atc = at < len ? at : len - 1;
-    constexpr int R = 32;
+    constexpr int R = 16;              // partials in flight per thread (256 partials per pass)
     float yh = 0.0f, yc = 0.0f;
     for (int k0 = s; k0 < o.nch; k0 += RS * R) {
         float v[R];

@@ -144,77 +144,82 @@ __global__ __launch_bounds__(THREADS) void k_compact(const uint64_t* __restrict_
 }
 
 // ===========================================================================
-// Predictor, second layer + threshold + union over tokens, one mask word (64
-// neurons) per workgroup.  Each wave owns 16 rows of P2t; 16 lanes share a row
-// (4 rows per load instruction, 256 contiguous bytes per row).  u is staged in
-// LDS per token group.
+// Predictor, second layer + threshold + union over tokens.  One workgroup per
+// 16 neurons, i.e. one 16-bit quarter of a mask word: small workgroups spread
+// the P2t rows evenly over the compute units whatever n is.  Each wave owns 4
+// rows and 16 lanes share a row (256 contiguous bytes per row per load).  A
+// row's first batch of loads is issued before u is staged in LDS, so the u
+// round trip overlaps the weight stream.  The workgroup writes its 16 mask bits
+// with one 16-bit store; the grid covers every quarter of every word, so the
+// tail bits past n are written as zeros.
 // ===========================================================================
+constexpr int L2_ROWS = 16;           // neurons per workgroup of k_pred_l2
+
 template <int WT, int BT>
 __global__ __launch_bounds__(THREADS) void k_pred_l2(const uint8_t* __restrict__ P2t,
                                                      const float* __restrict__ b2, float thr,
                                                      const float* __restrict__ u, int n, int r,
-                                                     int B, uint64_t* __restrict__ mask,
+                                                     int B, uint16_t* __restrict__ mask16,
                                                      float* __restrict__ logits) {
     constexpr int EPC = Chunk<WT>::EPC;
     constexpr int G = 16;                       // lanes per row
+    constexpr int U = 8;                        // chunks in flight per lane (a 2 KiB row at once)
     extern __shared__ float s_u[];              // [BT][r]
-    __shared__ unsigned s_flag[64];
+    __shared__ unsigned s_flag[L2_ROWS];
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     const int gi = lane / G, li = lane % G;
     const int nch = r / EPC;
-    const int64_t rb = row_bytes(WT, r);
-    if (threadIdx.x < 64) s_flag[threadIdx.x] = 0;
+    const int loc = 4 * wv + gi;                // neuron within the workgroup
+    const int i = L2_ROWS * blockIdx.x + loc;
+    const bool live = i < n;
+    const uint8_t* row = P2t + (int64_t)(live ? i : 0) * row_bytes(WT, r);
+    const float bias = (live && b2) ? b2[i] : 0.0f;
+    unsigned fire = 0;
     for (int b0 = 0; b0 < B; b0 += BT) {
         const int nb = min(BT, B - b0);
-        __syncthreads();
+        u4 w[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            if (live && li + G * q < nch) w[q] = ld16_stream(row + 16 * (int64_t)(li + G * q));
+        __syncthreads();                        // the previous group's reads of s_u are done
         for (int k = threadIdx.x; k < nb * r; k += THREADS) s_u[k] = u[(int64_t)b0 * r + k];
         for (int k = nb * r + threadIdx.x; k < BT * r; k += THREADS) s_u[k] = 0.0f;
         __syncthreads();
+        float acc[BT];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int loc = 16 * wv + 4 * p + gi;        // neuron within the word
-            const int i = 64 * blockIdx.x + loc;
-            float acc[BT];
+        for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
+        if (live) {
+            for (int c0 = li;;) {
 #pragma unroll
-            for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
-            if (i < n) {
-                const uint8_t* row = P2t + (int64_t)i * rb;
-                constexpr int U = 8;            // chunks in flight per lane (a 2 KiB row at once)
-                for (int c0 = li; c0 < nch; c0 += G * U) {
-                    u4 w[U];
+                for (int q = 0; q < U; ++q) {
+                    const int c = c0 + G * q;
+                    if (c < nch) {
 #pragma unroll
-                    for (int q = 0; q < U; ++q)
-                        if (c0 + G * q < nch) w[q] = ld16_stream(row + 16 * (int64_t)(c0 + G * q));
-#pragma unroll
-                    for (int q = 0; q < U; ++q) {
-                        const int c = c0 + G * q;
-                        if (c < nch) {
-#pragma unroll
-                            for (int b = 0; b < BT; ++b)
-                                acc[b] = Dot<WT, F32>::run(w[q], 0.0f, s_u + b * r + c * EPC,
-                                                           acc[b]);
-                        }
+                        for (int b = 0; b < BT; ++b)
+                            acc[b] = Dot<WT, F32>::run(w[q], 0.0f, s_u + b * r + c * EPC, acc[b]);
                     }
                 }
-            }
-            unsigned fire = 0;
-            const float bias = (i < n && b2) ? b2[i] : 0.0f;
+                c0 += G * U;
+                if (c0 >= nch) break;
 #pragma unroll
-            for (int b = 0; b < BT; ++b) {
-                float lg = group_sum<G>(acc[b]) + bias;
-                if (b < nb) {
-                    fire |= lg > thr;
-                    if (logits && li == 0 && i < n) logits[(int64_t)(b0 + b) * n + i] = lg;
-                }
+                for (int q = 0; q < U; ++q)
+                    if (c0 + G * q < nch) w[q] = ld16_stream(row + 16 * (int64_t)(c0 + G * q));
             }
-            if (li == 0 && i < n) s_flag[loc] |= fire;
+        }
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            const float lg = group_sum<G>(acc[b]) + bias;
+            if (b < nb) {
+                fire |= lg > thr;
+                if (logits && li == 0 && live) logits[(int64_t)(b0 + b) * n + i] = lg;
+            }
         }
     }
+    if (li == 0) s_flag[loc] = live ? fire : 0u;
     __syncthreads();
     if (wv == 0) {
-        const int i = 64 * blockIdx.x + lane;
-        uint64_t word = __ballot(i < n && s_flag[lane] != 0);
-        if (lane == 0) mask[blockIdx.x] = word;
+        const uint64_t bits = __ballot(lane < L2_ROWS && s_flag[lane & (L2_ROWS - 1)] != 0);
+        if (lane == 0) mask16[blockIdx.x] = (uint16_t)(bits & 0xffffu);
     }
 }
 
