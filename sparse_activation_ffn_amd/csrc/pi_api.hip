@@ -94,11 +94,23 @@ int mfma_chunks(int d) {
     return k < 2 ? 2 : k > NCH_MAX ? NCH_MAX : k;
 }
 
-size_t ws_pred_bytes(int r, int B) { return WS_CTR_BYTES + align256((size_t)B * r * 4); }
+// u [B][r], then (matrix-core predictor, B >= 16) the K-slice partials of x P1
+size_t ws_pred_bytes(int r, int B) {
+    size_t v = WS_CTR_BYTES + align256((size_t)B * r * 4);
+    if (B >= MFMA_MIN_BATCH) v += align256((size_t)P1_KS * B * r * 4);
+    return v;
+}
 
-// h [B][n] (gathered path only) and the partials of y
+// h: f32 [B][n] (gathered path) or f16 [B][mfma_h_ld(n)] (matrix-core path)
+int mfma_h_ld(int n) { return (n + 7) / 8 * 8 + 8; }
+size_t ws_h_bytes(int n, int B) {
+    const size_t f32 = (size_t)B * n * 4, f16 = (size_t)B * mfma_h_ld(n) * 2;
+    return align256(f32 > f16 ? f32 : f16);
+}
+
+// h and the partials of y
 size_t ws_ffn_bytes(int d, int n, int B, int nparts) {
-    return WS_CTR_BYTES + align256((size_t)B * n * 4) + align256((size_t)nparts * B * d * 4);
+    return WS_CTR_BYTES + ws_h_bytes(n, B) + align256((size_t)nparts * B * d * 4);
 }
 
 // ---- timing hooks --------------------------------------------------------------
@@ -233,15 +245,19 @@ pi_status launch_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
     return launch(PI_K_UP, k_up<WT, XT, BT, ACT, false>, dim3(grid), dim3(THREADS), mbytes, s, a);
 }
 
+// chunk partials -> y_hot, y_cold, y (one thread per 4 consecutive outputs)
+pi_status launch_reduce(const FfnArgs& a, const DownOut& o, hipStream_t s) {
+    const int64_t len4 = (int64_t)a.B * a.d / 4;
+    int grid = (int)((len4 + THREADS - 1) / THREADS);
+    if (grid > 4096) grid = 4096;
+    return launch(PI_K_REDUCE, k_reduce, dim3(grid), dim3(THREADS), 0, s, a, o);
+}
+
 template <int WT, int BT>
 pi_status launch_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     const int slices = (a.d + Down<WT>::COLS - 1) / Down<WT>::COLS;
-    pi_status st = launch(PI_K_DOWN, k_down<WT, BT>, dim3(slices, o.nch), dim3(THREADS), 0, s, a, o);
-    if (st != PI_OK) return st;
-    const int64_t len = (int64_t)a.B * a.d;
-    int grid = (int)((len + THREADS - 1) / THREADS);
-    if (grid > 2048) grid = 2048;
-    return launch(PI_K_REDUCE, k_reduce, dim3(grid), dim3(THREADS), 0, s, a, o);
+    TRY(launch(PI_K_DOWN, k_down<WT, BT>, dim3(slices, o.nch), dim3(THREADS), 0, s, a, o));
+    return launch_reduce(a, o, s);
 }
 
 template <int WT, int XT, int BT>
@@ -308,19 +324,23 @@ pi_status run_fused(const FfnArgs& a, const DownOut& o, int wt, int act, hipStre
 }
 
 // ---- matrix-core path -------------------------------------------------------
+template <int WT, int ACT>
+pi_status launch_mfma_up(const FfnArgs& a, int grid, hipStream_t s) {
+    const size_t sh = a.mask ? (size_t)(a.n + 63) / 64 * 8 : 0;   // mask words
+    auto kern = k_mfma_up<WT, ACT>;
+    TRY(allow_lds(kern, sh));
+    return launch(PI_K_UP, kern, dim3(grid), dim3(MFMA_WG), sh, s, a,
+                  reinterpret_cast<_Float16*>(a.h));
+}
+
 template <int WT>
 pi_status run_mfma_wt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
-    _Float16* h16 = reinterpret_cast<_Float16*>(a.h);
     const int ugrid = (rows_cap + UR - 1) / UR > 0 ? (rows_cap + UR - 1) / UR : 1;
-    if (act == PI_RELU)
-        TRY(launch(PI_K_UP, k_mfma_up<WT, RELU>, dim3(ugrid), dim3(256), 0, s, a, h16));
-    else
-        TRY(launch(PI_K_UP, k_mfma_up<WT, REGLU>, dim3(ugrid), dim3(256), 0, s, a, h16));
-    TRY(launch(PI_K_DOWN, k_mfma_down<WT>, dim3(a.d / DC, o.nch), dim3(256), 0, s, a, o,
-               (const _Float16*)h16));
-    const int64_t len = (int64_t)a.B * a.d;
-    return launch(PI_K_REDUCE, k_reduce_parts, dim3((unsigned)((len + RE - 1) / RE)),
-                  dim3(RE * RS), 0, s, a, o);
+    if (act == PI_RELU) TRY((launch_mfma_up<WT, RELU>(a, ugrid, s)));
+    else TRY((launch_mfma_up<WT, REGLU>(a, ugrid, s)));
+    TRY(launch(PI_K_DOWN, k_mfma_down<WT>, dim3(a.d / DC, o.nch), dim3(MFMA_WG), 0, s, a, o,
+               (const _Float16*)a.h));
+    return launch_reduce(a, o, s);
 }
 
 pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, int rows_cap,
@@ -385,7 +405,7 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
         CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
         Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),
                 const_cast<int32_t*>(counts)};
-        if (!mfma && (n + 63) / 64 <= MASK_WORDS_MAX) {
+        if ((n + 63) / 64 <= MASK_WORDS_MAX) {
             a.mask = mask;                   // compaction fused into k_ffn / k_up
             a.n = n;
             a.out_idx[0] = L.hot;
@@ -401,9 +421,11 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.rb = row_bytes(wt, d);
     a.x = (const uint8_t*)x;
     a.h = reinterpret_cast<float*>(base + WS_CTR_BYTES);
-    a.h_ld = n > 0 ? n : 1;
+    // f32 h [B][n] (gathered path) or f16 h [B][h_ld] (matrix-core path: hot
+    // items, then cold items from the next multiple of 8)
+    a.h_ld = mfma ? mfma_h_ld(n) : (n > 0 ? n : 1);
     DownOut o{};
-    o.partials = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * n * 4));
+    o.partials = reinterpret_cast<float*>(base + WS_CTR_BYTES + ws_h_bytes(n, B));
     o.y_part[0] = y0;
     o.y_part[1] = y1;
     o.y = y;
@@ -499,13 +521,26 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
     float* u = reinterpret_cast<float*>(base + WS_CTR_BYTES);
     hipStream_t s = (hipStream_t)stream;
     const int wt = p->wdtype;
-    pi_status st;
-    if (wt == F32)
-        st = xdtype == F32 ? pred_l1_bt<F32, F32>(p, x, B, u, s) : pred_l1_bt<F32, F16>(p, x, B, u, s);
-    else
-        st = xdtype == F32 ? pred_l1_bt<F16, F32>(p, x, B, u, s) : pred_l1_bt<F16, F16>(p, x, B, u, s);
-    TRY(st);
-    TRY(wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, s) : pred_l2_bt<F16>(p, u, B, mask, logits, s));
+    if (B >= MFMA_MIN_BATCH && wt == F16 && xdtype == F16 && p->r % PUK == 0) {
+        // matrix-core predictor: K-split first layer, slice sum + ReLU, second layer
+        float* part = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * p->r * 4));
+        TRY(launch(PI_K_PRED_L1, k_mfma_pred1, dim3((p->r + P1_ROWS - 1) / P1_ROWS, P1_KS), dim3(MFMA_WG),
+                   0, s, (const uint8_t*)p->P1t, (const uint8_t*)x, p->d, p->r, B, part));
+        const int64_t len = (int64_t)B * p->r;
+        int grid = (int)((len / 4 + THREADS - 1) / THREADS);
+        if (grid > 1024) grid = 1024;
+        TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(grid), dim3(THREADS), 0, s, (const float*)part, len, u));
+        TRY(launch(PI_K_PRED_L2, k_mfma_pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
+                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, p->n, p->r, B, mask, logits));
+    } else {
+        pi_status st;
+        if (wt == F32)
+            st = xdtype == F32 ? pred_l1_bt<F32, F32>(p, x, B, u, s) : pred_l1_bt<F32, F16>(p, x, B, u, s);
+        else
+            st = xdtype == F32 ? pred_l1_bt<F16, F32>(p, x, B, u, s) : pred_l1_bt<F16, F16>(p, x, B, u, s);
+        TRY(st);
+        TRY(wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, s) : pred_l2_bt<F16>(p, u, B, mask, logits, s));
+    }
     if (!lists) return PI_OK;
     return launch(PI_K_COMPACT, k_compact, dim3(1), dim3(THREADS), 0, s, (const uint64_t*)mask, p->n, L);
 }

@@ -598,33 +598,38 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
     }
 }
 
-// Reduction of the chunk partials, one thread per output element: the hot
-// chunks in order give y_hot, the cold chunks in order give y_cold, and
+// Reduction of the chunk partials, one thread per 4 consecutive outputs: the
+// hot chunks in order give y_hot, the cold chunks in order give y_cold, and
 // y = y_hot + y_cold is the merge.  Deterministic (fixed order, no atomics).
 __global__ __launch_bounds__(THREADS) void k_reduce(FfnArgs a, DownOut o) {
     int H, C;
     item_counts(a, H, C);
     int part, lo, hi, nh;
     chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
-    const int64_t len = (int64_t)a.B * a.d;
+    const int64_t len = (int64_t)a.B * a.d;           // a multiple of 4 (d % 64 == 0)
+    const int64_t len4 = len / 4;
     const int64_t stride = (int64_t)gridDim.x * THREADS;
-    constexpr int R = 32;      // partial loads in flight per thread (branch-free batches)
-    for (int64_t at = (int64_t)blockIdx.x * THREADS + threadIdx.x; at < len; at += stride) {
-        float yh = 0.0f, yc = 0.0f;
+    const f4* P = reinterpret_cast<const f4*>(o.partials);
+    constexpr int R = 8;       // partial loads in flight per thread (branch-free batches)
+    for (int64_t at = (int64_t)blockIdx.x * THREADS + threadIdx.x; at < len4; at += stride) {
+        f4 yh = {0.f, 0.f, 0.f, 0.f}, yc = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < o.nch; k0 += R) {
-            float v[R];
+            f4 v[R];
 #pragma unroll
-            for (int q = 0; q < R; ++q) v[q] = o.partials[min(k0 + q, o.nch - 1) * len + at];
+            for (int q = 0; q < R; ++q) v[q] = P[min(k0 + q, o.nch - 1) * len4 + at];
 #pragma unroll
             for (int q = 0; q < R; ++q) {
                 const int kk = k0 + q;
-                if (kk < nh) yh += v[q];
-                else if (kk < o.nch) yc += v[q];
+                if (kk < nh) {
+                    yh.x += v[q].x; yh.y += v[q].y; yh.z += v[q].z; yh.w += v[q].w;
+                } else if (kk < o.nch) {
+                    yc.x += v[q].x; yc.y += v[q].y; yc.z += v[q].z; yc.w += v[q].w;
+                }
             }
         }
-        if (o.y_part[0]) o.y_part[0][at] = yh;
-        if (o.y_part[1]) o.y_part[1][at] = yc;
-        if (o.y) o.y[at] = yh + yc;
+        if (o.y_part[0]) reinterpret_cast<f4*>(o.y_part[0])[at] = yh;
+        if (o.y_part[1]) reinterpret_cast<f4*>(o.y_part[1])[at] = yc;
+        if (o.y) reinterpret_cast<f4*>(o.y)[at] = f4{yh.x + yc.x, yh.y + yc.y, yh.z + yc.z, yh.w + yc.w};
     }
 }
 

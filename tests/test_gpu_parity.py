@@ -71,9 +71,9 @@ def check_step(Lh, n_hot, x_np, out, tokens=None):
     sel = (lambda a: a) if tokens is None else (lambda a: a[tokens])  # noqa: E731
     e = check_close(sel(out["y"]), y, Lh.wl.wdtype)
     if "y_hot" in out:
-        check_close(sel(out["y_hot"]), yh, Lh.wl.wdtype)
+        check_close(sel(out["y_hot"]), yh, Lh.wl.wdtype, scale=y)
         if out.get("y_cold") is not None:
-            check_close(sel(out["y_cold"]), yc, Lh.wl.wdtype)
+            check_close(sel(out["y_cold"]), yc, Lh.wl.wdtype, scale=y)
     return e, namb, len(hot_o) + len(cold_o)
 
 
@@ -146,11 +146,13 @@ MFMA_SMALL = {
     "reglu-f16": S.WORKLOADS["llama70b-reglu-fp16"].scaled(d=768, n=1333, r=64),
     "relu-f16-split": S.WORKLOADS["opt30b-fp16"].scaled(d=512, n=1500, r=32),
     "q4_0": S.WORKLOADS["opt175b-q4_0"].scaled(d=1280, n=1111, r=64),
+    "q4_0-reglu-split": S.WORKLOADS["opt175b-q4_0"].scaled(d=768, n=900, r=32, act="reglu",
+                                                           hot_frac=0.3, name="q4_0-reglu-small"),
 }
 
 
 @pytest.mark.parametrize("name,B", [("reglu-f16", 16), ("reglu-f16", 33), ("relu-f16-split", 64),
-                                    ("q4_0", 20), ("q4_0", 64)])
+                                    ("q4_0", 20), ("q4_0", 64), ("q4_0-reglu-split", 48)])
 def test_matrix_core_batches(name, B):
     """Batches of 16..64 tokens (matrix-core path): union active set, f16-rounded h and
     dequantised weights, checked to the fp16 / Q4_0 tolerance."""
