@@ -87,7 +87,8 @@ constexpr int MFMA_MIN_BATCH = 16;
 bool use_mfma(int d, int wt, int xt, int B) {
     return B >= MFMA_MIN_BATCH && B <= MM && xt == F16 && (wt == F16 || wt == Q4) && d % DC == 0;
 }
-// split-K chunks of the MFMA down kernel: about 512 workgroups in total
+// split-K chunks of the matrix-core down kernel: about two workgroups per
+// compute unit
 int mfma_chunks(int d) {
     const int tiles = d / DC;
     const int k = 512 / (tiles > 0 ? tiles : 1);
@@ -324,22 +325,52 @@ pi_status run_fused(const FfnArgs& a, const DownOut& o, int wt, int act, hipStre
 }
 
 // ---- matrix-core path -------------------------------------------------------
-template <int WT, int ACT>
-pi_status launch_mfma_up(const FfnArgs& a, int grid, hipStream_t s) {
+// token tiles of 16 covering the batch (1, 2 or 4)
+int mfma_mt(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
+
+template <typename K>
+pi_status launch_up_kernel(K kern, const FfnArgs& a, int rows_cap, hipStream_t s) {
+    constexpr int UR = 64;                             // items per workgroup
+    const int grid = rows_cap > 0 ? (rows_cap + UR - 1) / UR : 1;
     const size_t sh = a.mask ? (size_t)(a.n + 63) / 64 * 8 : 0;   // mask words
-    auto kern = k_mfma_up<WT, ACT>;
     TRY(allow_lds(kern, sh));
     return launch(PI_K_UP, kern, dim3(grid), dim3(MFMA_WG), sh, s, a,
                   reinterpret_cast<_Float16*>(a.h));
 }
 
+template <int WT, int ACT, int MT>
+pi_status launch_mfma_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
+    return launch_up_kernel(k_mfma_up<WT, ACT, MT, 1>, a, rows_cap, s);
+}
+
+template <int WT, int ACT>
+pi_status mfma_up_mt(const FfnArgs& a, int rows_cap, hipStream_t s) {
+    switch (mfma_mt(a.B)) {
+    case 1: return launch_mfma_up<WT, ACT, 1>(a, rows_cap, s);
+    case 2: return launch_mfma_up<WT, ACT, 2>(a, rows_cap, s);
+    default: return launch_mfma_up<WT, ACT, 4>(a, rows_cap, s);
+    }
+}
+
+template <int WT, bool LISTS, int MT>
+pi_status mfma_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
+    return launch(PI_K_DOWN, k_mfma_down<WT, LISTS, MT>, dim3(a.d / DC, o.nch), dim3(DOWN_WG), 0, s, a,
+                  o, (const _Float16*)a.h);
+}
+
 template <int WT>
 pi_status run_mfma_wt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
-    const int ugrid = (rows_cap + UR - 1) / UR > 0 ? (rows_cap + UR - 1) / UR : 1;
-    if (act == PI_RELU) TRY((launch_mfma_up<WT, RELU>(a, ugrid, s)));
-    else TRY((launch_mfma_up<WT, REGLU>(a, ugrid, s)));
-    TRY(launch(PI_K_DOWN, k_mfma_down<WT>, dim3(a.d / DC, o.nch), dim3(MFMA_WG), 0, s, a, o,
-               (const _Float16*)a.h));
+    if (act == PI_RELU) TRY((mfma_up_mt<WT, RELU>(a, rows_cap, s)));
+    else TRY((mfma_up_mt<WT, REGLU>(a, rows_cap, s)));
+    const bool lists = a.idx[0] || a.idx[1];          // else dense rows
+    switch (mfma_mt(a.B) * 2 + (lists ? 1 : 0)) {
+    case 2: TRY((mfma_down<WT, false, 1>(a, o, s))); break;
+    case 3: TRY((mfma_down<WT, true, 1>(a, o, s))); break;
+    case 4: TRY((mfma_down<WT, false, 2>(a, o, s))); break;
+    case 5: TRY((mfma_down<WT, true, 2>(a, o, s))); break;
+    case 8: TRY((mfma_down<WT, false, 4>(a, o, s))); break;
+    default: TRY((mfma_down<WT, true, 4>(a, o, s))); break;
+    }
     return launch_reduce(a, o, s);
 }
 
@@ -521,16 +552,20 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
     float* u = reinterpret_cast<float*>(base + WS_CTR_BYTES);
     hipStream_t s = (hipStream_t)stream;
     const int wt = p->wdtype;
-    if (B >= MFMA_MIN_BATCH && wt == F16 && xdtype == F16 && p->r % PUK == 0) {
+    if (B >= MFMA_MIN_BATCH && wt == F16 && xdtype == F16 && p->r % KS == 0 && p->d % KS == 0) {
         // matrix-core predictor: K-split first layer, slice sum + ReLU, second layer
         float* part = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * p->r * 4));
-        TRY(launch(PI_K_PRED_L1, k_mfma_pred1, dim3((p->r + P1_ROWS - 1) / P1_ROWS, P1_KS), dim3(MFMA_WG),
-                   0, s, (const uint8_t*)p->P1t, (const uint8_t*)x, p->d, p->r, B, part));
+        const dim3 g1((p->r + P1_ROWS - 1) / P1_ROWS, P1_KS);
+        const int mt = mfma_mt(B);
+        auto pred1 = mt == 1 ? k_mfma_pred1<1> : mt == 2 ? k_mfma_pred1<2> : k_mfma_pred1<4>;
+        TRY(launch(PI_K_PRED_L1, pred1, g1, dim3(MFMA_WG), 0, s, (const uint8_t*)p->P1t,
+                   (const uint8_t*)x, p->d, p->r, B, part));
         const int64_t len = (int64_t)B * p->r;
         int grid = (int)((len / 4 + THREADS - 1) / THREADS);
         if (grid > 1024) grid = 1024;
         TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(grid), dim3(THREADS), 0, s, (const float*)part, len, u));
-        TRY(launch(PI_K_PRED_L2, k_mfma_pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
+        auto pred2 = mt == 1 ? k_mfma_pred2<1> : mt == 2 ? k_mfma_pred2<2> : k_mfma_pred2<4>;
+        TRY(launch(PI_K_PRED_L2, pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
                    (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, p->n, p->r, B, mask, logits));
     } else {
         pi_status st;

@@ -12,7 +12,12 @@
 // read each) and receives D[m = 4 q + i][n = c] for i = 0..3.  Any numbering of
 // k works as long as A and B agree, which they do by construction.
 //
-// Both kernels are software-pipelined: the global loads of step s + D are
+// Every LDS operand tile has 256-byte rows (128 f16 of K) whose sixteen 16-byte
+// blocks are XOR-swizzled by the row index (swz): a fragment read (16 rows,
+// one block each per 16 lanes) and the staging stores used here touch every
+// bank once, where rows padded by 16 bytes measure 2-way conflicts on gfx950.
+//
+// All kernels are software-pipelined: the global loads of step s + D are
 // issued into a register ring right after step s's registers are written to
 // LDS, so D steps of weights are in flight while the matrix cores work.
 //
@@ -27,12 +32,15 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4m __attribute__((ext_vector_type(4)));
 
-constexpr int MM = 64;          // tokens per tile (batch padded to 64)
-constexpr int UR = 128;         // active rows per up workgroup (32 per wave)
+constexpr int MM = 64;          // largest token tile (batches up to 64)
+constexpr int KS = 128;         // K per pipeline step: one 256-byte LDS row
 constexpr int DC = 128;         // output columns per down workgroup (32 per wave)
 constexpr int DK = 128;         // active rows (K) per down step
-constexpr int LP = 8;           // LDS row padding in halves (keeps 16-byte alignment)
-constexpr int MFMA_WG = 256;    // threads of both kernels (4 waves)
+constexpr int MFMA_WG = 256;    // threads of the up and predictor kernels (4 waves)
+constexpr int DOWN_WG = 256;    // threads of the down kernel (4 waves)
+
+// Byte offset of 16-byte block kb (0..15) of row r in a [rows][256 B] tile.
+__device__ __forceinline__ int swz(int r, int kb) { return r * 256 + 16 * (kb ^ (r & 15)); }
 
 __device__ __forceinline__ f4m mfma32(h8 a, h8 b, f4m c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -92,61 +100,74 @@ __device__ __forceinline__ int h_pos(int item, int H) { return item < H ? item :
 
 // Software pipeline over K steps [s0, s1): D stages of global loads in a
 // register ring; step s's registers go to LDS, then step s + D is loaded into
-// the freed registers while the matrix cores work on step s.
-template <int D, typename Stage, typename Load, typename Store, typename Compute>
+// the freed registers while the matrix cores work on step s.  The loop body is
+// the same on every path: every stage issues the same loads (past the end it
+// reloads the last step), and the padding steps of the last round are stored
+// with their token operand zeroed (store(R, false)) and computed, adding exact
+// zeros.  The compiler's wait counts are then static inside a round, so a store
+// waits only for its own stage, never for the D - 1 stages issued after it.
+template <int D, typename Stage, int ROUND = 12 / D * D, typename Load, typename Store, typename Compute>
 __device__ __forceinline__ void run_pipeline(int s0, int s1, Load load, Store store, Compute compute) {
+    if (s1 <= s0) return;                             // uniform
     Stage R[D];
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd)
-        if (s0 + dd < s1) load(R[dd], s0 + dd);
-    for (int sb = s0; sb < s1; sb += D) {
+    for (int dd = 0; dd < D; ++dd) load(R[dd], min(s0 + dd, s1 - 1));
+    // the compiler cannot carry exact wait counts around a loop back edge (it
+    // waits for everything at the loop head), so a round is several rings long
+    static_assert(ROUND % D == 0, "a round is whole rings");
+    for (int sb = s0; sb < s1; sb += ROUND) {
 #pragma unroll
-        for (int dd = 0; dd < D; ++dd) {
+        for (int dd = 0; dd < ROUND; ++dd) {
             const int s = sb + dd;
-            if (s < s1) {
-                __syncthreads();                      // the previous step's LDS reads are done
-                store(R[dd]);
-                if (s + D < s1) load(R[dd], s + D);
-                __syncthreads();
-                compute();
-            }
+            __syncthreads();                          // the previous step's LDS reads are done
+            store(R[dd % D], s < s1);
+            load(R[dd % D], min(s + D, s1 - 1));
+            __syncthreads();
+            compute();
         }
     }
 }
 
 // ===========================================================================
-// Up/gate.  Workgroup = 4 waves; tile = 64 tokens x 128 items (32 per wave).
-// A step stages K = CH chunks of every row (Q4_0: CH blocks of 32; f16: CH x 8
-// elements) and the matching 64 x K slice of x.  With a mask the workgroup
-// scans it (all of it, in LDS) and resolves its own 128 items; workgroup 0
-// writes the counts and every workgroup its items of the ascending lists.
-// Writes h (f16) [B][h_ld] at h_pos(item).
+// Up/gate.  Workgroup = 4 waves; tile = 16 MT tokens x UR = 64 NT items (16 NT
+// per wave).  A step stages K = 128 of every row (Q4_0: 4 blocks of 32; f16:
+// 16 chunks of 8) and the matching token x K slice of x.  With a mask the
+// workgroup scans it (all of it, in LDS) and resolves its own UR items;
+// workgroup 0 writes the counts and every workgroup its items of the ascending
+// lists.  Writes h (f16) [B][h_ld] at h_pos(item).
 // ===========================================================================
-template <int WT, int NM> struct UpShape {
-    static constexpr int EPC = WT == Q4 ? 32 : 8;      // weights per 16-byte chunk
-    static constexpr int CH = WT == Q4 ? 4 : 8;        // chunks per row per step
-    static constexpr int UK = CH * EPC;                // K per step (128 or 64)
+template <int WT, int MT, int NT> struct UpShape {
+    static constexpr int CH = WT == Q4 ? 4 : 16;       // 16-byte chunks per row per step
+    static constexpr int UR = 64 * NT;                 // items per workgroup
     static constexpr int J = UR * CH / MFMA_WG;        // chunks per thread per matrix
-    static constexpr int XJ = MM * UK / 8 / MFMA_WG;   // 16-byte x loads per thread
+    static constexpr int XN = 16 * MT * 16;            // 16-byte pieces of the x slice
+    static constexpr int XJ = (XN + MFMA_WG - 1) / MFMA_WG;
     static constexpr int D = 3;                        // steps in flight
 };
 
-template <int WT, int ACT>
-__global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __restrict__ h16) {
-    constexpr int NM = ACT == REGLU ? 2 : 1;
-    using S = UpShape<WT, NM>;
-    constexpr int UK = S::UK, CH = S::CH, J = S::J, XJ = S::XJ, D = S::D;
-    __shared__ __attribute__((aligned(16))) _Float16 s_x[MM][UK + LP];
-    __shared__ __attribute__((aligned(16))) _Float16 s_w[NM][UR][UK + LP];
-    __shared__ int s_row[UR];
-    __shared__ int s_part[UR];
-    __shared__ int s_cnt[2];
-    extern __shared__ uint64_t s_words[];        // mask words (mask mode only)
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int q = lane >> 4, c = lane & 15;
-    const int i0 = blockIdx.x * UR;
+// Chunk t of a step -> (row, chunk).  f16: 16 lanes cover one row's 256 bytes;
+// Q4_0: 16 lanes cover one block of 16 rows, so each of the 4 stores of a
+// dequantised block hits 16 different swizzled positions.
+template <int WT>
+__device__ __forceinline__ void up_task(int t, int& r, int& ch) {
+    if (WT == Q4) {
+        r = (t & 15) + 16 * (t >> 6);
+        ch = (t >> 4) & 3;
+    } else {
+        r = t >> 4;
+        ch = t & 15;
+    }
+}
 
-    int H, C;
+// Items [i0, i0 + UR) of an up workgroup -> s_row / s_part (row -1: not a row).
+// With a mask the workgroup scans all of it in LDS (s_words) and emits its own
+// items; workgroup 0 writes the counts and every workgroup its items of the
+// ascending lists.  Returns false (uniformly) when the workgroup has no items.
+template <int UR>
+__device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, uint64_t* s_words,
+                           int& H, int& C) {
+    __shared__ int s_cnt[2];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (a.mask) {
         // block-wide scan of the mask words: thread t owns words [t per, t per + per)
         const int words = (a.n + 63) / 64;
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
         __syncthreads();
     } else {
         item_counts(a, H, C);
-        if (i0 >= H + C) return;                          // whole workgroup, uniformly
+        if (i0 >= H + C) return false;                    // whole workgroup, uniformly
         if (tid < UR) {
             const int item = min(i0 + tid, H + C - 1);
             int part, row;
@@ -228,106 +249,19 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
         }
         __syncthreads();
     }
-    const int T = H + C;
-    if (i0 >= T) return;                                  // whole workgroup, uniformly
+    return i0 < H + C;
+}
 
-    // per-thread weight sources: chunk j of matrix g is (row r = t / CH, chunk t % CH)
-    const uint8_t* src[NM][J];
-    bool live[J];
+// Bias, activation and the f16 h write of an up tile: lane holds
+// acc[g][jn][mt][i] = D[token 16 mt + 4 q + i][item 16 NT wv + 16 jn + c].
+template <int ACT, int NM, int NT, int MT>
+__device__ __forceinline__ void up_epilogue(const FfnArgs& a, const f4m (&acc)[NM][NT][MT], const int* s_row,
+                                            const int* s_part, int i0, int H, int T, _Float16* __restrict__ h16) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int q = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int t = tid + MFMA_WG * j, r = t / CH;
-        const int row = s_row[r], part = s_part[r];
-        live[j] = row >= 0;
-        // a row that is not one (an out-of-range id) reads row 0 of a partition
-        // that has rows, and its weights are zeroed
-        const int rr = row >= 0 ? row : 0;
-        const int pp = row >= 0 ? part : (a.rows[0] > 0 ? 0 : 1);
-        src[0][j] = a.up[pp] + (int64_t)rr * a.rb;
-        if (NM == 2) src[NM - 1][j] = a.gate[pp] + (int64_t)rr * a.rb;
-    }
-    struct Stage {
-        u4 w[NM][J];
-        _Float16 sc[NM][J];
-        u4 xv[XJ];
-    };
-    auto load = [&](Stage& R, int s) {
-        const int k0 = s * UK;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int ch = (tid + MFMA_WG * j) % CH;
-#pragma unroll
-            for (int g = 0; g < NM; ++g) {
-                if (WT == Q4) {
-                    const int blk = k0 / 32 + ch;
-                    R.w[g][j] = ld16_stream(src[g][j] + 16 * (int64_t)blk);
-                    R.sc[g][j] = __builtin_bit_cast(
-                        _Float16, *reinterpret_cast<const uint16_t*>(src[g][j] + a.d / 2 + 2 * (int64_t)blk));
-                } else {
-                    R.w[g][j] = ld16_stream(src[g][j] + 2 * (int64_t)(k0 + 8 * ch));
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (UK / 8), e = (t % (UK / 8)) * 8;
-            R.xv[j] = m < a.B ? ld16(a.x + ((int64_t)m * a.d + k0 + e) * 2) : u4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store = [&](const Stage& R) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int t = tid + MFMA_WG * j, r = t / CH, ch = t % CH;
-#pragma unroll
-            for (int g = 0; g < NM; ++g) {
-                if (WT == Q4) {
-                    u4 o[4];
-                    deq_block(R.w[g][j], live[j] ? R.sc[g][j] : (_Float16)0.0f, o);
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) *reinterpret_cast<u4*>(&s_w[g][r][32 * ch + 8 * p]) = o[p];
-                } else {
-                    *reinterpret_cast<u4*>(&s_w[g][r][8 * ch]) = live[j] ? R.w[g][j] : u4{0u, 0u, 0u, 0u};
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (UK / 8), e = (t % (UK / 8)) * 8;
-            *reinterpret_cast<u4*>(&s_x[m][e]) = R.xv[j];
-        }
-    };
-    f4m acc[NM][2][4];
-#pragma unroll
-    for (int g = 0; g < NM; ++g)
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) acc[g][jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&]() {
-#pragma unroll
-        for (int ks = 0; ks < UK / 32; ++ks) {
-            const int kk = 32 * ks + 8 * q;
-            h8 ax[4], bw[NM][2];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) ax[mt] = *reinterpret_cast<const h8*>(&s_x[16 * mt + c][kk]);
-#pragma unroll
-            for (int g = 0; g < NM; ++g)
-#pragma unroll
-                for (int jn = 0; jn < 2; ++jn)
-                    bw[g][jn] = *reinterpret_cast<const h8*>(&s_w[g][32 * wv + 16 * jn + c][kk]);
-#pragma unroll
-            for (int g = 0; g < NM; ++g)
-#pragma unroll
-                for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) acc[g][jn][mt] = mfma32(ax[mt], bw[g][jn], acc[g][jn][mt]);
-        }
-    };
-    run_pipeline<D, Stage>(0, a.d / UK, load, store, compute);
-    // epilogue: lane holds D[token 16 mt + 4 q + i][item 32 wv + 16 jn + c]
-#pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-        const int r = 32 * wv + 16 * jn + c;
+    for (int jn = 0; jn < NT; ++jn) {
+        const int r = 16 * NT * wv + 16 * jn + c;
         const int row = s_row[r], part = s_part[r];
         const int item = i0 + r;
         if (item < T) {
@@ -335,7 +269,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
             const float bu = (row >= 0 && a.bup[part]) ? a.bup[part][row] : 0.0f;
             const float bg = (ACT == REGLU && row >= 0 && a.bgate[part]) ? a.bgate[part][row] : 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = 16 * mt + 4 * q + i;
@@ -357,6 +291,124 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
     }
 }
 
+template <int WT, int ACT, int MT, int NT>
+__global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __restrict__ h16) {
+    constexpr int NM = ACT == REGLU ? 2 : 1;
+    using S = UpShape<WT, MT, NT>;
+    constexpr int J = S::J, XN = S::XN, XJ = S::XJ, D = S::D, UR = S::UR;
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[16 * MT * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[NM][UR * 256];
+    __shared__ int s_row[UR];
+    __shared__ int s_part[UR];
+    extern __shared__ uint64_t s_words[];        // mask words (mask mode only)
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int q = lane >> 4, c = lane & 15;
+    const int i0 = blockIdx.x * UR;
+
+    int H, C;
+    if (!up_resolve<UR>(a, i0, s_row, s_part, s_words, H, C)) return;
+    const int T = H + C;
+
+    // per-thread weight sources (a row that is not one, an out-of-range id,
+    // reads row 0 of a partition that has rows, and its weights are zeroed)
+    const uint8_t* src[NM][J];
+    bool live[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        int r, ch;
+        up_task<WT>(tid + MFMA_WG * j, r, ch);
+        const int row = s_row[r], part = s_part[r];
+        live[j] = row >= 0;
+        const int rr = row >= 0 ? row : 0;
+        const int pp = row >= 0 ? part : (a.rows[0] > 0 ? 0 : 1);
+        src[0][j] = a.up[pp] + (int64_t)rr * a.rb;
+        if (NM == 2) src[NM - 1][j] = a.gate[pp] + (int64_t)rr * a.rb;
+    }
+    struct Stage {
+        u4 w[NM][J];
+        _Float16 sc[NM][J];
+        u4 xv[XJ];
+    };
+    auto load = [&](Stage& R, int s) {
+        const int k0 = s * KS;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            int r, ch;
+            up_task<WT>(tid + MFMA_WG * j, r, ch);
+#pragma unroll
+            for (int g = 0; g < NM; ++g) {
+                if (WT == Q4) {
+                    const int blk = k0 / 32 + ch;
+                    R.w[g][j] = ld16_stream(src[g][j] + 16 * (int64_t)blk);
+                    R.sc[g][j] = __builtin_bit_cast(
+                        _Float16, *reinterpret_cast<const uint16_t*>(src[g][j] + a.d / 2 + 2 * (int64_t)blk));
+                } else {
+                    R.w[g][j] = ld16_stream(src[g][j] + 2 * (int64_t)(k0 + 8 * ch));
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const int t = min(tid + MFMA_WG * j, XN - 1), m = t >> 4, kb = t & 15;
+            R.xv[j] = ld16(a.x + ((int64_t)min(m, a.B - 1) * a.d + k0 + 8 * kb) * 2);
+        }
+    };
+    // (zeroing of padding tokens and of non-rows happens here, where the data
+    // are consumed: a select right after a load would make the load wait)
+    auto store = [&](const Stage& R, bool act) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            int r, ch;
+            up_task<WT>(tid + MFMA_WG * j, r, ch);
+#pragma unroll
+            for (int g = 0; g < NM; ++g) {
+                if (WT == Q4) {
+                    u4 o[4];
+                    deq_block(R.w[g][j], live[j] ? R.sc[g][j] : (_Float16)0.0f, o);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) *reinterpret_cast<u4*>(s_w[g] + swz(r, 4 * ch + p)) = o[p];
+                } else {
+                    *reinterpret_cast<u4*>(s_w[g] + swz(r, ch)) = live[j] ? R.w[g][j] : u4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const int t = tid + MFMA_WG * j, m = t >> 4, kb = t & 15;
+            if (t < XN) *reinterpret_cast<u4*>(s_x + swz(m, kb)) = (act && m < a.B) ? R.xv[j] : u4{0u, 0u, 0u, 0u};
+        }
+    };
+    f4m acc[NM][NT][MT];
+#pragma unroll
+    for (int g = 0; g < NM; ++g)
+#pragma unroll
+        for (int jn = 0; jn < NT; ++jn)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[g][jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KS / 32; ++ks) {
+            const int kb = 4 * ks + q;
+            h8 ax[MT], bw[NM][NT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) ax[mt] = *reinterpret_cast<const h8*>(s_x + swz(16 * mt + c, kb));
+#pragma unroll
+            for (int g = 0; g < NM; ++g)
+#pragma unroll
+                for (int jn = 0; jn < NT; ++jn)
+                    bw[g][jn] = *reinterpret_cast<const h8*>(s_w[g] + swz(16 * NT * wv + 16 * jn + c, kb));
+#pragma unroll
+            for (int g = 0; g < NM; ++g)
+#pragma unroll
+                for (int jn = 0; jn < NT; ++jn)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[g][jn][mt] = mfma32(ax[mt], bw[g][jn], acc[g][jn][mt]);
+        }
+    };
+    run_pipeline<D, Stage>(0, a.d / KS, load, store, compute);
+    up_epilogue<ACT, NM, NT, MT>(a, acc, s_row, s_part, i0, H, T, h16);
+}
+
 // Split of one partition's items over chunks, chunk starts on multiples of 8.
 __device__ __forceinline__ void chunk_range8(int nch, int H, int C, int k, int& part, int& lo,
                                              int& hi) {
@@ -374,27 +426,32 @@ __device__ __forceinline__ void chunk_range8(int nch, int H, int C, int k, int& 
 // ===========================================================================
 // Down, split over K (the active rows): grid (d / 128 column tiles, chunks);
 // chunk k covers the items chunk_range8 gives it (one partition).  A step
-// stages 128 rows x 128 columns of W_downT and the 64 x 128 tile of h.  Each
-// thread loads an 8 x 8 block of weights (8 rows x 16 bytes) and transposes it
-// in registers, so every LDS column holds 8 consecutive rows in 16 bytes; the
-// column's 16-byte blocks are XOR-swizzled so both the stores and the MFMA
-// reads are free of bank conflicts.
+// stages 128 rows x 128 columns of W_downT and the token x 128 tile of h.
+// Each thread loads an 8 x 8 block of weights (8 rows x 16 bytes; the 16
+// lanes of a load group read 256 contiguous bytes of one row) and transposes
+// it in registers, so every LDS column (a 256-byte row of the tile) holds the
+// step's 128 rows.  4 waves, each owning 32 columns.
 // ===========================================================================
-__device__ __forceinline__ int wt_off(int col, int kb) {          // halves
-    return col * DK + 8 * (kb ^ ((col & 15) ^ ((col >> 3) & 15)));
+// Byte offset of 16-byte block kb of column col in the transposed weight tile:
+// the block index is XOR-ed with the column and its column group, so the
+// stores (16 lanes = 16 column groups of one row block) and the fragment reads
+// (16 consecutive columns) both spread over the banks.
+__device__ __forceinline__ int wt_off(int col, int kb) {
+    return col * 256 + 16 * (kb ^ ((col & 15) ^ ((col >> 3) & 15)));
 }
 
-template <int WT> struct DownShape {
-    static constexpr int HJ = MM * DK / 8 / MFMA_WG;  // 16-byte h loads per thread
-    static constexpr int D = WT == Q4 ? 3 : 2;        // steps in flight
+template <int WT, int MT> struct DownShape {
+    static constexpr int HN = 16 * MT * 16;                    // 16-byte pieces of the h tile
+    static constexpr int HJ = (HN + DOWN_WG - 1) / DOWN_WG;    // per thread
+    static constexpr int D = WT == Q4 ? 3 : 2;                 // steps in flight
 };
 
-template <int WT>
-__global__ __launch_bounds__(MFMA_WG) void k_mfma_down(FfnArgs a, DownOut o, const _Float16* __restrict__ h16) {
-    using S = DownShape<WT>;
-    constexpr int HJ = S::HJ, D = S::D;
-    __shared__ __attribute__((aligned(16))) _Float16 s_h[MM][DK + LP];
-    __shared__ __attribute__((aligned(16))) _Float16 s_wt[DC * DK];       // [column][k], swizzled
+template <int WT, bool LISTS, int MT>
+__global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, const _Float16* __restrict__ h16) {
+    using S = DownShape<WT, MT>;
+    constexpr int HN = S::HN, HJ = S::HJ, D = S::D;
+    __shared__ __attribute__((aligned(16))) uint8_t s_h[16 * MT * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_wt[DC * 256];      // [column][k], swizzled
     __shared__ __attribute__((aligned(16))) int s_ids[D + 1][DK];        // row ids of upcoming steps
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
@@ -411,130 +468,131 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_down(FfnArgs a, DownOut o, con
     // this thread's 8 x 8 weight block: rows 8 rg .. +7 of the step, columns 8 cg .. +7
     const int cg = tid & 15, rg = tid >> 4;
     const int col0 = c0 + 8 * cg;
-    // row id of step-relative item tid of step s (threads tid < DK), or -1
-    auto row_id = [&](int s) -> int {
-        const int item = lo + s * DK + tid;
-        if (tid >= DK || item >= hi) return -1;
-        const int row = idx ? idx[item] : item;
-        return (unsigned)row < (unsigned)prows ? row : -1;
-    };
-    struct Stage {
-        u4 w[8];                      // f16: 8 columns of each of 8 rows
-        u2 cq[8];                     // Q4_0: 8 codes of each of 8 rows
-        _Float16 sc[8];
-        u4 hv[HJ];
-    };
-    // loads of step s; its row ids are in s_ids[s % (D + 1)]
-    auto load = [&](Stage& R, int s) {
-        const int* ids = s_ids[s % (D + 1)];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int row = ids[8 * rg + r];
-            const uint8_t* rowp = base + (int64_t)(row >= 0 ? row : 0) * a.rb;
-            if (WT == Q4) {
-                const int blk = col0 >> 5, t0 = col0 & 31;
-                R.cq[r] = *reinterpret_cast<const u2*>(rowp + 16 * (int64_t)blk + (t0 & 15));
-                const _Float16 sv = __builtin_bit_cast(
-                    _Float16, *reinterpret_cast<const uint16_t*>(rowp + a.d / 2 + 2 * (int64_t)blk));
-                R.sc[r] = row >= 0 ? sv : (_Float16)0.0f;
-            } else {
-                const u4 v = ld16_stream(rowp + 2 * (int64_t)col0);
-                R.w[r] = row >= 0 ? v : u4{0u, 0u, 0u, 0u};
-            }
-        }
-        const int i0 = lo + s * DK;
-#pragma unroll
-        for (int j = 0; j < HJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (DK / 8), e = (t % (DK / 8)) * 8;
-            u4 v = u4{0u, 0u, 0u, 0u};
-            if (m < a.B && i0 + e < hi) {
-                v = ld16(h16 + (int64_t)m * a.h_ld + hb + i0 + e);
-                const int valid = hi - (i0 + e);           // items past hi are zero
-                if (valid < 8) {
-                    unsigned w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        if (2 * p >= valid) w4[p] = 0u;
-                        else if (2 * p + 1 >= valid) w4[p] &= 0xffffu;
-                    }
-                    v = u4{w4[0], w4[1], w4[2], w4[3]};
-                }
-            }
-            R.hv[j] = v;
-        }
-    };
-    auto store = [&](const Stage& R) {
-        unsigned V[8][4];                               // V[r][p] = columns 2p, 2p+1 of row r
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            u4 w;
-            if (WT == Q4) w = deq8(R.cq[r], R.sc[r], (col0 & 31) >= 16);
-            else w = R.w[r];
-            V[r][0] = w.x; V[r][1] = w.y; V[r][2] = w.z; V[r][3] = w.w;
-        }
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-            const int p = cc >> 1;
-            const unsigned sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-            u4 out;
-            out.x = __builtin_amdgcn_perm(V[1][p], V[0][p], sel);
-            out.y = __builtin_amdgcn_perm(V[3][p], V[2][p], sel);
-            out.z = __builtin_amdgcn_perm(V[5][p], V[4][p], sel);
-            out.w = __builtin_amdgcn_perm(V[7][p], V[6][p], sel);
-            *reinterpret_cast<u4*>(&s_wt[wt_off(8 * cg + cc, rg)]) = out;
-        }
-#pragma unroll
-        for (int j = 0; j < HJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (DK / 8), e = (t % (DK / 8)) * 8;
-            *reinterpret_cast<u4*>(&s_h[m][e]) = R.hv[j];
-        }
-    };
-    f4m acc[2][4];
+    f4m acc[2][MT];
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&]() {
+        for (int mt = 0; mt < MT; ++mt) acc[jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
+    if (steps > 0) {                                  // uniform; an empty chunk writes zeros
+        // row id of step-relative item tid of step s, or -1 (loads a clamped,
+        // valid list entry whatever s is, so the load is unconditional)
+        auto row_id = [&](int s) -> int {
+            const int item = lo + s * DK + tid;
+            const int ic = min(item, hi - 1);
+            const int v = LISTS ? idx[ic] : ic;
+            return (tid < DK && item < hi && (unsigned)v < (unsigned)prows) ? v : -1;
+        };
+        struct Stage {
+            u4 w[8];                  // f16: 8 columns of each of 8 rows
+            u2 cq[8];                 // Q4_0: 8 codes of each of 8 rows
+            _Float16 sc[8];
+            u4 hv[HJ];
+            unsigned rows_ok;         // bit r: row r is a row (else its weights are zeroed)
+            int hvalid[HJ];           // items of each h load that are in the chunk
+        };
+        // loads of step s (its row ids are in s_ids[s % (D + 1)]); all unconditional
+        auto load = [&](Stage& R, int s) {
+            const int* ids = s_ids[s % (D + 1)];
+            R.rows_ok = 0;
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-            h8 ah[4], bw[2];
+            for (int r = 0; r < 8; ++r) {
+                const int row = ids[8 * rg + r];
+                R.rows_ok |= (row >= 0 ? 1u : 0u) << r;
+                const uint8_t* rowp = base + (int64_t)(row >= 0 ? row : 0) * a.rb;
+                if (WT == Q4) {
+                    const int blk = col0 >> 5, t0 = col0 & 31;
+                    R.cq[r] = *reinterpret_cast<const u2*>(rowp + 16 * (int64_t)blk + (t0 & 15));
+                    R.sc[r] = __builtin_bit_cast(
+                        _Float16, *reinterpret_cast<const uint16_t*>(rowp + a.d / 2 + 2 * (int64_t)blk));
+                } else {
+                    R.w[r] = ld16_stream(rowp + 2 * (int64_t)col0);
+                }
+            }
+            const int i0 = lo + s * DK;
+            const int last = round8(hi) - 8;          // last 8-item group of this chunk
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                ah[mt] = *reinterpret_cast<const h8*>(&s_h[16 * mt + c][32 * ks + 8 * q]);
+            for (int j = 0; j < HJ; ++j) {
+                const int t = min(tid + DOWN_WG * j, HN - 1), m = t >> 4, kb = t & 15;
+                R.hv[j] = ld16(h16 + (int64_t)min(m, a.B - 1) * a.h_ld + hb + min(i0 + 8 * kb, last));
+                R.hvalid[j] = m < a.B ? hi - (i0 + 8 * kb) : 0;   // items past hi are zero
+            }
+        };
+        auto store = [&](const Stage& R, bool act) {
+            unsigned V[8][4];                           // V[r][p] = columns 2p, 2p+1 of row r
 #pragma unroll
-            for (int jn = 0; jn < 2; ++jn)
-                bw[jn] = *reinterpret_cast<const h8*>(&s_wt[wt_off(32 * wv + 16 * jn + c, 4 * ks + q)]);
+            for (int r = 0; r < 8; ++r) {
+                const bool ok = (R.rows_ok >> r) & 1u;
+                u4 w;
+                if (WT == Q4) w = deq8(R.cq[r], ok ? R.sc[r] : (_Float16)0.0f, (col0 & 31) >= 16);
+                else w = ok ? R.w[r] : u4{0u, 0u, 0u, 0u};
+                V[r][0] = w.x; V[r][1] = w.y; V[r][2] = w.z; V[r][3] = w.w;
+            }
 #pragma unroll
-            for (int jn = 0; jn < 2; ++jn)
+            for (int cc = 0; cc < 8; ++cc) {
+                const int p = cc >> 1;
+                const unsigned sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                u4 out;
+                out.x = __builtin_amdgcn_perm(V[1][p], V[0][p], sel);
+                out.y = __builtin_amdgcn_perm(V[3][p], V[2][p], sel);
+                out.z = __builtin_amdgcn_perm(V[5][p], V[4][p], sel);
+                out.w = __builtin_amdgcn_perm(V[7][p], V[6][p], sel);
+                *reinterpret_cast<u4*>(s_wt + wt_off(8 * cg + cc, rg)) = out;
+            }
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) acc[jn][mt] = mfma32(ah[mt], bw[jn], acc[jn][mt]);
-        }
-    };
-    // prologue: ids of the first D steps, then their loads; the id of step D is
-    // loaded into a register (ids run one step ahead of the weights, and each id
-    // load is issued before the weight loads it must not wait behind)
+            for (int j = 0; j < HJ; ++j) {
+                const int t = tid + DOWN_WG * j, m = t >> 4, kb = t & 15;
+                const u4 v = R.hv[j];
+                const int valid = act ? R.hvalid[j] : 0;
+                if (t < HN)
+                    *reinterpret_cast<u4*>(s_h + swz(m, kb)) =
+                        u4{valid >= 2 ? v.x : (valid == 1 ? v.x & 0xffffu : 0u),
+                           valid >= 4 ? v.y : (valid == 3 ? v.y & 0xffffu : 0u),
+                           valid >= 6 ? v.z : (valid == 5 ? v.z & 0xffffu : 0u),
+                           valid >= 8 ? v.w : (valid == 7 ? v.w & 0xffffu : 0u)};
+            }
+        };
+        auto compute = [&]() {
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd)
-        if (tid < DK) s_ids[dd][tid] = row_id(dd);
-    __syncthreads();
-    int nid = row_id(D);
-    Stage R[D];
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const int kb = 4 * ks + q;
+                h8 ah[MT], bw[2];
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd)
-        if (dd < steps) load(R[dd], dd);
-    for (int s0 = 0; s0 < steps; s0 += D) {
+                for (int mt = 0; mt < MT; ++mt) ah[mt] = *reinterpret_cast<const h8*>(s_h + swz(16 * mt + c, kb));
+#pragma unroll
+                for (int jn = 0; jn < 2; ++jn)
+                    bw[jn] = *reinterpret_cast<const h8*>(s_wt + wt_off(32 * wv + 16 * jn + c, kb));
+#pragma unroll
+                for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[jn][mt] = mfma32(ah[mt], bw[jn], acc[jn][mt]);
+            }
+        };
+        // ids run one step ahead of the weights: the id load of step s + D + 1
+        // is issued before the weight loads of step s + D, so waiting for it
+        // never waits behind them
 #pragma unroll
         for (int dd = 0; dd < D; ++dd) {
-            const int s = s0 + dd;
-            if (s < steps) {
+            const int v = row_id(dd);
+            if (tid < DK) s_ids[dd][tid] = v;
+        }
+        __syncthreads();
+        int nid = row_id(D);
+        Stage R[D];
+#pragma unroll
+        for (int dd = 0; dd < D; ++dd) load(R[dd], min(dd, steps - 1));
+        constexpr int ROUND = D;                  // one ring per round (see run_pipeline)
+        for (int sb = 0; sb < steps; sb += ROUND) {
+#pragma unroll
+            for (int dd = 0; dd < ROUND; ++dd) {
+                // same body on every path (see run_pipeline): padding steps of
+                // the last round store a zero h tile and add exact zeros
+                const int s = sb + dd;
                 __syncthreads();                      // the previous step's LDS reads are done
-                store(R[dd]);
+                store(R[dd % D], s < steps);
                 if (tid < DK) s_ids[(s + D) % (D + 1)][tid] = nid;
                 __syncthreads();
-                if (s + D < steps) {
-                    nid = row_id(s + D + 1);
-                    load(R[dd], s + D);
-                }
+                nid = row_id(s + D + 1);
+                load(R[dd % D], min(s + D, steps - 1));
                 compute();
             }
         }
@@ -544,7 +602,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_down(FfnArgs a, DownOut o, con
     for (int jn = 0; jn < 2; ++jn) {
         const int col = c0 + 32 * wv + 16 * jn + c;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * mt + 4 * q + i;
@@ -563,16 +621,17 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_down(FfnArgs a, DownOut o, con
 // ===========================================================================
 constexpr int P1_ROWS = 64;     // P1t rows per workgroup (16 per wave)
 constexpr int P1_KS = 16;       // K slices
-constexpr int PUK = 64;         // K per step (8 chunks of 8 f16 per row)
 
+template <int MT>
 __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred1(const uint8_t* __restrict__ P1t,
                                                        const uint8_t* __restrict__ x, int d, int r,
                                                        int B, float* __restrict__ part) {
-    constexpr int J = P1_ROWS * (PUK / 8) / MFMA_WG;  // 16-byte weight loads per thread
-    constexpr int XJ = MM * PUK / 8 / MFMA_WG;        // 16-byte x loads per thread
+    constexpr int J = P1_ROWS * 16 / MFMA_WG;         // 16-byte weight loads per thread
+    constexpr int XN = 16 * MT * 16;                  // 16-byte pieces of the x slice
+    constexpr int XJ = (XN + MFMA_WG - 1) / MFMA_WG;  // per thread
     constexpr int D = 3;
-    __shared__ __attribute__((aligned(16))) _Float16 s_x[MM][PUK + LP];
-    __shared__ __attribute__((aligned(16))) _Float16 s_w[P1_ROWS][PUK + LP];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[16 * MT * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[P1_ROWS * 256];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
     const int j0 = blockIdx.x * P1_ROWS, ky = blockIdx.y;
@@ -581,7 +640,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred1(const uint8_t* __restric
     bool live[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int row = j0 + (tid + MFMA_WG * j) / (PUK / 8);
+        const int row = j0 + ((tid + MFMA_WG * j) >> 4);
         live[j] = row < r;
         src[j] = P1t + (int64_t)(row < r ? row : 0) * rb;
     }
@@ -590,50 +649,47 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred1(const uint8_t* __restric
         u4 xv[XJ];
     };
     auto load = [&](Stage& R, int s) {
-        const int k0 = s * PUK;
+        const int k0 = s * KS;
+#pragma unroll
+        for (int j = 0; j < J; ++j) R.w[j] = ld16_stream(src[j] + 2 * (int64_t)(k0 + 8 * ((tid + MFMA_WG * j) & 15)));
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const int t = min(tid + MFMA_WG * j, XN - 1), m = t >> 4, kb = t & 15;
+            R.xv[j] = ld16(x + ((int64_t)min(m, B - 1) * d + k0 + 8 * kb) * 2);
+        }
+    };
+    auto store = [&](const Stage& R, bool act) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int ch = (tid + MFMA_WG * j) % (PUK / 8);
-            R.w[j] = ld16_stream(src[j] + 2 * (int64_t)(k0 + 8 * ch));
+            const int t = tid + MFMA_WG * j;
+            *reinterpret_cast<u4*>(s_w + swz(t >> 4, t & 15)) = live[j] ? R.w[j] : u4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < XJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (PUK / 8), e = (t % (PUK / 8)) * 8;
-            R.xv[j] = m < B ? ld16(x + ((int64_t)m * d + k0 + e) * 2) : u4{0u, 0u, 0u, 0u};
+            const int t = tid + MFMA_WG * j, m = t >> 4, kb = t & 15;
+            if (t < XN) *reinterpret_cast<u4*>(s_x + swz(m, kb)) = (act && m < B) ? R.xv[j] : u4{0u, 0u, 0u, 0u};
         }
     };
-    auto store = [&](const Stage& R) {
+    f4m acc[MT];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int t = tid + MFMA_WG * j, rr = t / (PUK / 8), ch = t % (PUK / 8);
-            *reinterpret_cast<u4*>(&s_w[rr][8 * ch]) = live[j] ? R.w[j] : u4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (PUK / 8), e = (t % (PUK / 8)) * 8;
-            *reinterpret_cast<u4*>(&s_x[m][e]) = R.xv[j];
-        }
-    };
-    f4m acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f4m{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f4m{0.f, 0.f, 0.f, 0.f};
     auto compute = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < PUK / 32; ++ks) {
-            const int kk = 32 * ks + 8 * q;
-            const h8 bw = *reinterpret_cast<const h8*>(&s_w[16 * wv + c][kk]);
+        for (int ks = 0; ks < KS / 32; ++ks) {
+            const int kb = 4 * ks + q;
+            const h8 bw = *reinterpret_cast<const h8*>(s_w + swz(16 * wv + c, kb));
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = mfma32(*reinterpret_cast<const h8*>(&s_x[16 * mt + c][kk]), bw, acc[mt]);
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = mfma32(*reinterpret_cast<const h8*>(s_x + swz(16 * mt + c, kb)), bw, acc[mt]);
         }
     };
-    const int steps = d / PUK;
+    const int steps = d / KS;
     run_pipeline<D, Stage>(ky * steps / P1_KS, (ky + 1) * steps / P1_KS, load, store, compute);
     // lane holds D[token 16 mt + 4 q + i][row 16 wv + c]
     const int row = j0 + 16 * wv + c;
     if (row < r) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * mt + 4 * q + i;
@@ -670,17 +726,19 @@ __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ pa
 // ===========================================================================
 constexpr int P2_ROWS = 128;    // neurons per workgroup (32 per wave)
 
+template <int MT>
 __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restrict__ P2t,
                                                        const float* __restrict__ b2, float thr,
                                                        const float* __restrict__ u, int n, int r,
                                                        int B, uint64_t* __restrict__ mask,
                                                        float* __restrict__ logits) {
-    constexpr int J = P2_ROWS * (PUK / 8) / MFMA_WG;  // 16-byte weight loads per thread
-    constexpr int UJ = MM * PUK / 4 / MFMA_WG;        // 16-byte (4 float) u loads per thread
-    constexpr int D = 3;
-    __shared__ __attribute__((aligned(16))) _Float16 s_uh[MM][PUK + LP];
-    __shared__ __attribute__((aligned(16))) _Float16 s_ul[MM][PUK + LP];
-    __shared__ __attribute__((aligned(16))) _Float16 s_w[P2_ROWS][PUK + LP];
+    constexpr int J = P2_ROWS * 16 / MFMA_WG;         // 16-byte weight loads per thread
+    constexpr int UN = 16 * MT * 16;                  // 8-float pieces of the u slice
+    constexpr int UJ = (UN + MFMA_WG - 1) / MFMA_WG;  // per thread
+    constexpr int D = 2;
+    __shared__ __attribute__((aligned(16))) uint8_t s_uh[16 * MT * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ul[16 * MT * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[P2_ROWS * 256];
     __shared__ unsigned s_flag[P2_ROWS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
@@ -690,67 +748,69 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
     bool live[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int row = i0 + (tid + MFMA_WG * j) / (PUK / 8);
+        const int row = i0 + ((tid + MFMA_WG * j) >> 4);
         live[j] = row < n;
         src[j] = P2t + (int64_t)(row < n ? row : 0) * rb;
     }
     struct Stage {
         u4 w[J];
-        f4 uv[UJ];
+        f4 uv[UJ][2];
     };
     auto load = [&](Stage& R, int s) {
-        const int k0 = s * PUK;
+        const int k0 = s * KS;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int ch = (tid + MFMA_WG * j) % (PUK / 8);
-            R.w[j] = ld16_stream(src[j] + 2 * (int64_t)(k0 + 8 * ch));
-        }
+        for (int j = 0; j < J; ++j) R.w[j] = ld16_stream(src[j] + 2 * (int64_t)(k0 + 8 * ((tid + MFMA_WG * j) & 15)));
 #pragma unroll
         for (int j = 0; j < UJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (PUK / 4), e = (t % (PUK / 4)) * 4;
-            R.uv[j] = m < B ? *reinterpret_cast<const f4*>(u + (int64_t)m * r + k0 + e) : f4{0.f, 0.f, 0.f, 0.f};
+            const int t = min(tid + MFMA_WG * j, UN - 1), m = t >> 4, kb = t & 15;
+            const f4* up = reinterpret_cast<const f4*>(u + (int64_t)min(m, B - 1) * r + k0 + 8 * kb);
+            R.uv[j][0] = up[0];
+            R.uv[j][1] = up[1];
         }
     };
-    auto store = [&](const Stage& R) {
+    auto store = [&](const Stage& R, bool act) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int t = tid + MFMA_WG * j, rr = t / (PUK / 8), ch = t % (PUK / 8);
-            *reinterpret_cast<u4*>(&s_w[rr][8 * ch]) = live[j] ? R.w[j] : u4{0u, 0u, 0u, 0u};
+            const int t = tid + MFMA_WG * j;
+            *reinterpret_cast<u4*>(s_w + swz(t >> 4, t & 15)) = live[j] ? R.w[j] : u4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < UJ; ++j) {
-            const int t = tid + MFMA_WG * j, m = t / (PUK / 4), e = (t % (PUK / 4)) * 4;
-            const float v[4] = {R.uv[j].x, R.uv[j].y, R.uv[j].z, R.uv[j].w};
-            _Float16 hi[4], lo[4];
+            const int t = tid + MFMA_WG * j, m = t >> 4, kb = t & 15;
+            if (t < UN) {
+                const bool ok = act && m < B;
+                const float v[8] = {R.uv[j][0].x, R.uv[j][0].y, R.uv[j][0].z, R.uv[j][0].w,
+                                    R.uv[j][1].x, R.uv[j][1].y, R.uv[j][1].z, R.uv[j][1].w};
+                unsigned hw[4], lw[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                hi[p] = (_Float16)v[p];
-                lo[p] = (_Float16)(v[p] - (float)hi[p]);
+                for (int p = 0; p < 4; ++p) {
+                    const float a0 = ok ? v[2 * p] : 0.0f, a1 = ok ? v[2 * p + 1] : 0.0f;
+                    const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+                    const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
+                    hw[p] = (unsigned)__builtin_bit_cast(uint16_t, h0) | ((unsigned)__builtin_bit_cast(uint16_t, h1) << 16);
+                    lw[p] = (unsigned)__builtin_bit_cast(uint16_t, l0) | ((unsigned)__builtin_bit_cast(uint16_t, l1) << 16);
+                }
+                *reinterpret_cast<u4*>(s_uh + swz(m, kb)) = u4{hw[0], hw[1], hw[2], hw[3]};
+                *reinterpret_cast<u4*>(s_ul + swz(m, kb)) = u4{lw[0], lw[1], lw[2], lw[3]};
             }
-            *reinterpret_cast<u2*>(&s_uh[m][e]) =
-                u2{(unsigned)__builtin_bit_cast(uint16_t, hi[0]) | ((unsigned)__builtin_bit_cast(uint16_t, hi[1]) << 16),
-                   (unsigned)__builtin_bit_cast(uint16_t, hi[2]) | ((unsigned)__builtin_bit_cast(uint16_t, hi[3]) << 16)};
-            *reinterpret_cast<u2*>(&s_ul[m][e]) =
-                u2{(unsigned)__builtin_bit_cast(uint16_t, lo[0]) | ((unsigned)__builtin_bit_cast(uint16_t, lo[1]) << 16),
-                   (unsigned)__builtin_bit_cast(uint16_t, lo[2]) | ((unsigned)__builtin_bit_cast(uint16_t, lo[3]) << 16)};
         }
     };
-    f4m acc[2][4];
+    f4m acc[2][MT];
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc[jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
     auto compute = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < PUK / 32; ++ks) {
-            const int kk = 32 * ks + 8 * q;
+        for (int ks = 0; ks < KS / 32; ++ks) {
+            const int kb = 4 * ks + q;
             h8 bw[2];
 #pragma unroll
-            for (int jn = 0; jn < 2; ++jn) bw[jn] = *reinterpret_cast<const h8*>(&s_w[32 * wv + 16 * jn + c][kk]);
+            for (int jn = 0; jn < 2; ++jn) bw[jn] = *reinterpret_cast<const h8*>(s_w + swz(32 * wv + 16 * jn + c, kb));
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const h8 ah = *reinterpret_cast<const h8*>(&s_uh[16 * mt + c][kk]);
-                const h8 al = *reinterpret_cast<const h8*>(&s_ul[16 * mt + c][kk]);
+            for (int mt = 0; mt < MT; ++mt) {
+                const h8 ah = *reinterpret_cast<const h8*>(s_uh + swz(16 * mt + c, kb));
+                const h8 al = *reinterpret_cast<const h8*>(s_ul + swz(16 * mt + c, kb));
 #pragma unroll
                 for (int jn = 0; jn < 2; ++jn) {
                     acc[jn][mt] = mfma32(ah, bw[jn], acc[jn][mt]);
@@ -759,7 +819,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
             }
         }
     };
-    run_pipeline<D, Stage>(0, r / PUK, load, store, compute);
+    run_pipeline<D, Stage, 8>(0, r / KS, load, store, compute);     // r = 1024: one round
     // lane holds D[token 16 mt + 4 q + i][neuron 32 wv + 16 jn + c]
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
@@ -767,7 +827,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
         const float bias = (i < n && b2) ? b2[i] : 0.0f;
         unsigned fire = 0;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tok = 16 * mt + 4 * q + e;
