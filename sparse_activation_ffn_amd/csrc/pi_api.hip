@@ -69,10 +69,11 @@ int fused_nc(int d, int wt) {
     return nc <= 1 ? 1 : nc <= 2 ? 2 : nc <= 4 ? 4 : 0;
 }
 
-// The fused path takes batches up to 4 with the natural x dtype of the weights,
-// where its double-buffered rows and accumulators fit in registers (Q4_0:
-// batch 1 and d <= 16384; four chunks per thread: batch 1); other shapes take
-// the gathered two-kernel path.
+// The fused path takes batch 1, and batches up to 4 that the matrix-core path
+// does not take (f32 weights), with the natural x dtype of the weights, where
+// its double-buffered rows and accumulators fit in registers (Q4_0: batch 1 and
+// d <= 16384; four chunks per thread: batch 1); other shapes take the gathered
+// two-kernel path.
 bool use_fused(int d, int wt, int xt, int B) {
     const bool pair = (wt == F32 && xt == F32) || (wt != F32 && xt == F16);
     const int nc = fused_nc(d, wt);
@@ -82,8 +83,11 @@ bool use_fused(int d, int wt, int xt, int B) {
     return true;
 }
 
-// Matrix-core path: batches of 16..64 tokens with f16 x and f16 / Q4_0 weights.
-constexpr int MFMA_MIN_BATCH = 16;
+// Matrix-core path: batches of 2..64 tokens with f16 x and f16 / Q4_0 weights
+// (measured faster than the fused kernel from batch 2 on: at batch 4 of the
+// ReGLU 70B layer 130 vs 163 us per layer step; at batch 1 the fused kernel
+// wins, 48 vs 77 us on the OPT-30B layer).
+constexpr int MFMA_MIN_BATCH = 2;
 bool use_mfma(int d, int wt, int xt, int B) {
     return B >= MFMA_MIN_BATCH && B <= MM && xt == F16 && (wt == F16 || wt == Q4) && d % DC == 0;
 }
@@ -407,8 +411,8 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     }
     const int d = hot->d, wt = hot->wdtype;
     const int n = hot->rows + (has_cold ? cold->rows : 0);
-    const bool fused = use_fused(d, wt, xdtype, B);
-    const bool mfma = !fused && use_mfma(d, wt, xdtype, B);
+    const bool mfma = use_mfma(d, wt, xdtype, B);
+    const bool fused = !mfma && use_fused(d, wt, xdtype, B);
     const int nch = fused ? NWG_FUSED : mfma ? mfma_chunks(d) : pick_nch(d, wt, B);
     TRY(check_ws(ws, ws_bytes, ws_ffn_bytes(d, n, B, nch)));
 
