@@ -228,7 +228,9 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
             // reduction slots alternate so each group needs one barrier
             struct Regs {
                 u4 wu[G][NC], wg[G][NC], wd[G][NC];
-                float su[G][NC], sg[G][NC], sd[G][NC];
+                // Q4_0 scales stay raw f16 bits until they are used: converting
+                // right after the load would make the next group's loads wait
+                uint16_t su[G][NC], sg[G][NC], sd[G][NC];
                 int row[G];
             };
             auto load_group = [&](Regs& R, int g0) {
@@ -255,10 +257,10 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
 #pragma unroll
                         for (int k = 0; k < NC; ++k) {
                             const int c = min(tid + FT * k, nch - 1);
-                            R.su[g][k] = half_f(*(const uint16_t*)(wup + sbase + 2 * c));
+                            R.su[g][k] = *(const uint16_t*)(wup + sbase + 2 * c);
                             if (ACT == REGLU)
-                                R.sg[g][k] = half_f(*(const uint16_t*)(wgt + sbase + 2 * c));
-                            R.sd[g][k] = half_f(*(const uint16_t*)(wdn + sbase + 2 * c));
+                                R.sg[g][k] = *(const uint16_t*)(wgt + sbase + 2 * c);
+                            R.sd[g][k] = *(const uint16_t*)(wdn + sbase + 2 * c);
                         }
                     }
                 }
@@ -275,9 +277,9 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                             const int c = tid + FT * k;
                             if (c < nch) {
                                 const uint8_t* xp = s_x + b * xrow + (int64_t)c * EPC * XB;
-                                pu = Dot<WT, XT>::run(R.wu[g][k], WT == Q4 ? R.su[g][k] : 0.f, xp, pu);
+                                pu = Dot<WT, XT>::run(R.wu[g][k], WT == Q4 ? half_f(R.su[g][k]) : 0.f, xp, pu);
                                 if (ACT == REGLU)
-                                    pg = Dot<WT, XT>::run(R.wg[g][k], WT == Q4 ? R.sg[g][k] : 0.f, xp,
+                                    pg = Dot<WT, XT>::run(R.wg[g][k], WT == Q4 ? half_f(R.sg[g][k]) : 0.f, xp,
                                                           pg);
                             }
                         }
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         if (r < 0 || b >= nb) hv = 0.0f;
 #pragma unroll
                         for (int k = 0; k < NC; ++k)
-                            Axpy<WT>::run(R.wd[g][k], WT == Q4 ? R.sd[g][k] : 0.f, hv, acc[b][k]);
+                            Axpy<WT>::run(R.wd[g][k], WT == Q4 ? half_f(R.sd[g][k]) : 0.f, hv, acc[b][k]);
                     }
                 }
             };

@@ -151,11 +151,13 @@ MFMA_SMALL = {
 }
 
 
-@pytest.mark.parametrize("name,B", [("reglu-f16", 16), ("reglu-f16", 33), ("relu-f16-split", 64),
+@pytest.mark.parametrize("name,B", [("relu-f16-split", 2), ("reglu-f16", 3), ("q4_0", 5),
+                                    ("reglu-f16", 16), ("reglu-f16", 33), ("relu-f16-split", 64),
                                     ("q4_0", 20), ("q4_0", 64), ("q4_0-reglu-split", 48)])
 def test_matrix_core_batches(name, B):
-    """Batches of 16..64 tokens (matrix-core path): union active set, f16-rounded h and
-    dequantised weights, checked to the fp16 / Q4_0 tolerance."""
+    """Batches of 2..64 tokens (matrix-core path: token tiles of 16, 32 and 64): union
+    active set, f16-rounded h and dequantised weights, checked to the fp16 / Q4_0
+    tolerance."""
     wl = MFMA_SMALL[name]
     log(f"matrix-core {name} B={B}")
     L = S.make_layer(wl)
@@ -169,6 +171,27 @@ def test_matrix_core_batches(name, B):
         x = S.make_x(wl, 0, step, B)
         e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step == 0)))
         log(f"  step {step}: union active {na}, ambiguous {namb}, err {e:.2e}")
+
+
+@pytest.mark.parametrize("B", [2, 20])
+@pytest.mark.parametrize("thr", [1e30, -1e30])
+def test_matrix_core_empty_and_full_active_sets(thr, B):
+    """Matrix-core path with no active neuron (y = 0 exactly, zero counts) and with
+    every neuron active (y = dense FFN), both partitions present."""
+    import dataclasses
+    wl = MFMA_SMALL["relu-f16-split"]
+    L = dataclasses.replace(S.make_layer(wl), threshold=thr)
+    dl = DeviceLayer.upload(L, DEV, n_hot=600)
+    buf = StepBuffers(dl, B, DEV)
+    x = S.make_x(wl, 0, 0, B)
+    out = run_step(dl, buf, x)
+    if thr > 0:
+        assert out["counts"].tolist() == [0, 0] and not out["mask"].any()
+        assert np.all(out["y"] == 0) and np.all(out["y_hot"] == 0) and np.all(out["y_cold"] == 0)
+    else:
+        assert out["counts"].tolist() == [600, wl.n - 600]
+        check_close(out["y"], O.dense_ffn(O.Part.from_layer(L), x), "f16")
+    check_step(L, 600, x, out)
 
 
 def test_fp32_layer_all_decode_tokens():
