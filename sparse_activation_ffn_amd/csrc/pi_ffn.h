@@ -231,13 +231,24 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                 // Q4_0 scales stay raw f16 bits until they are used: converting
                 // right after the load would make the next group's loads wait
                 uint16_t su[G][NC], sg[G][NC], sd[G][NC];
+                float bu[G], bg[G];                    // biases of the group's rows
                 int row[G];
             };
+            // the biases are loaded with the group's weights: a load consumed
+            // right away would make the wait before this group also wait for the
+            // next group's loads, which are in flight by then
+            const float* bsu = bup ? bup : reinterpret_cast<const float*>(a.x);
+            const float* bsg = bgt ? bgt : reinterpret_cast<const float*>(a.x);
             auto load_group = [&](Regs& R, int g0) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int r = s_row[min(g0 + g, len - 1)];
                     R.row[g] = g0 + g < len ? r : -1;
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    R.bu[g] = bsu[bup ? max(R.row[g], 0) : 0];
+                    if (ACT == REGLU) R.bg[g] = bsg[bgt ? max(R.row[g], 0) : 0];
                 }
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
@@ -296,8 +307,8 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int r = R.row[g];
-                    const float bu = (r >= 0 && bup) ? bup[r] : 0.0f;
-                    const float bg = (ACT == REGLU && r >= 0 && bgt) ? bgt[r] : 0.0f;
+                    const float bu = (r >= 0 && bup) ? R.bu[g] : 0.0f;
+                    const float bg = (ACT == REGLU && r >= 0 && bgt) ? R.bg[g] : 0.0f;
 #pragma unroll
                     for (int b = 0; b < BT; ++b) {
                         float up = 0.0f, gt = 0.0f;
