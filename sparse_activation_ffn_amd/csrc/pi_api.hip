@@ -62,6 +62,9 @@ int pick_nch(int d, int wt, int B) {
 constexpr int NWG_FUSED = PI_FFN_WORKGROUPS;
 constexpr int FUSED_MAX_BATCH = 4;
 
+// token tile of the batch-templated kernels
+int batch_tile(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
 // 16-byte chunks per thread of k_ffn for rows of d elements (1, 2 or 4; 0 = too wide)
 int fused_nc(int d, int wt) {
     const int epc = wt == F32 ? 4 : wt == F16 ? 8 : 32;
@@ -78,6 +81,9 @@ bool use_fused(int d, int wt, int xt, int B) {
     const bool pair = (wt == F32 && xt == F32) || (wt != F32 && xt == F16);
     const int nc = fused_nc(d, wt);
     if (!pair || B > FUSED_MAX_BATCH || nc == 0) return false;
+    // x of the token tile, the mask words and the static LDS
+    const size_t lds = (size_t)batch_tile(B) * d * (xt == F32 ? 4 : 2) + 8 * (size_t)MASK_WORDS_MAX + 4096;
+    if (lds > 160 * 1024) return false;
     if (wt == Q4 && (B > 1 || nc == 4)) return false;
     if (nc == 4 && B > 1) return false;
     return true;
@@ -142,8 +148,6 @@ pi_status launch(int kid, K kernel, dim3 grid, dim3 block, size_t shmem, hipStre
         return fail(PI_ERR_HIP, "%s launch: %s", pi_kernel_name(kid), hipGetErrorString(e));
     return PI_OK;
 }
-
-int batch_tile(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
 
 // ---- argument checks ----------------------------------------------------------------
 pi_status check_dtype_x(int xdtype) {

@@ -238,4 +238,10 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<WAVE>(v); }
 
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
 }  // namespace pi

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     __shared__ int s_row[FSTAGE];
     __shared__ float s_red[2][FW][G][NM][BT];
     __shared__ int s_wtot[FW];
-    __shared__ int s_hot;
+    __shared__ int s_whot[FW];
     const int64_t xrow = (int64_t)a.d * XB;
     uint8_t* s_x = s_dyn;
     uint64_t* s_words = reinterpret_cast<uint64_t*>(s_dyn + BT * xrow);
@@ -85,75 +85,80 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     const int wv = tid / WAVE;
     const int nch = a.d / EPC;                         // 16-byte (code) chunks of a row
 
-    // Prologue, one memory round trip: this thread's run of mask words and its
-    // share of x are loaded together, before anything waits on either.
+    // Prologue, one memory round trip: this thread's share of x and its run of
+    // mask words are loaded before anything waits on either (x first, so the
+    // wait at the join after the conditional mask loads covers both).
     constexpr int PMAX = (MASK_WORDS_MAX + FT - 1) / FT;
+    constexpr int XCH = BT * NC * EPC * XB / 16;       // 16-byte x pieces per thread (d <= NC FT EPC)
     const int words = a.mask ? (a.n + 63) / 64 : 0;
     const int per = (words + FT - 1) / FT;             // mask words per thread (<= PMAX)
     const int w0 = tid * per;
+    const int all16 = (int)(BT * xrow / 16);
+    auto load_x = [&](u4 (&xv)[XCH], int b0) {
+        const int n16 = (int)(min(BT, a.B - b0) * xrow / 16);
+        const u4* src = reinterpret_cast<const u4*>(a.x + b0 * xrow);
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) xv[j] = src[min(tid + FT * j, n16 - 1)];
+    };
+    auto store_x = [&](const u4 (&xv)[XCH], int b0) {
+        const int n16 = (int)(min(BT, a.B - b0) * xrow / 16);
+        u4* dst = reinterpret_cast<u4*>(s_x);
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int k = tid + FT * j;
+            if (k < all16) dst[k] = k < n16 ? xv[j] : u4{0u, 0u, 0u, 0u};
+        }
+    };
+    u4 xv0[XCH];
+    load_x(xv0, 0);
     uint64_t mw[PMAX];
 #pragma unroll
     for (int q = 0; q < PMAX; ++q) {
         mw[q] = 0;
-        if (q < per && w0 + q < words) mw[q] = a.mask[w0 + q];
+        if (q < per) mw[q] = a.mask[min(w0 + q, words - 1)];
     }
-    {
-        const int nb = min(BT, a.B);
-        const u4* src = reinterpret_cast<const u4*>(a.x);
-        u4* dst = reinterpret_cast<u4*>(s_x);
-        const int n16 = (int)(nb * xrow / 16), all16 = (int)(BT * xrow / 16);
-        for (int k = tid; k < all16; k += FT) dst[k] = k < n16 ? src[k] : u4{0u, 0u, 0u, 0u};
-    }
+    store_x(xv0, 0);
     int H, C;
     int run = 0;                                       // rank of this thread's first set bit
     if (a.mask) {
-        if (a.n % 64) {                                // bits past n are not neurons
-#pragma unroll
-            for (int q = 0; q < PMAX; ++q)
-                if (q < per && w0 + q == words - 1) mw[q] &= (1ull << (a.n % 64)) - 1ull;
-        }
-        int tot = 0;
+        // per-thread totals and counts below n_hot (hot ranks are [0, H))
+        const int nhot = a.rows[0];
+        int tot = 0, hot = 0;
 #pragma unroll
         for (int q = 0; q < PMAX; ++q) {
-            tot += __popcll(mw[q]);
-            if (q < per && w0 + q < words) s_words[w0 + q] = mw[q];   // for the row emission
+            if (q < per) {
+                const int w = w0 + q;
+                uint64_t v = w < words ? mw[q] : 0ull;
+                if (w == words - 1 && a.n % 64) v &= (1ull << (a.n % 64)) - 1ull;   // bits past n
+                tot += __popcll(v);
+                hot += 64 * w + 64 <= nhot ? __popcll(v)
+                       : 64 * w < nhot     ? __popcll(v & ((1ull << (nhot - 64 * w)) - 1ull))
+                                           : 0;
+                if (w < words) s_words[w] = v;         // read back by this thread only
+            }
         }
         // exclusive scan of the per-thread totals: shuffles in the wave, then the
-        // FW wave totals through LDS
+        // FW wave totals through LDS; the hot counts are only summed
         int inc = tot;
 #pragma unroll
         for (int o = 1; o < WAVE; o <<= 1) {
             const int v = __shfl_up(inc, o, WAVE);
             if (lane >= o) inc += v;
         }
+        hot = wave_sum_int(hot);
         if (lane == WAVE - 1) s_wtot[wv] = inc;
-        // the thread holding bit nhot of the mask finds H (hot ranks are [0, H))
-        const int nhot = a.rows[0];
+        if (lane == 0) s_whot[wv] = hot;
         __syncthreads();
         int before = 0, T = 0;
+        H = 0;
 #pragma unroll
         for (int w = 0; w < FW; ++w) {
             const int t = s_wtot[w];
             before += w < wv ? t : 0;
             T += t;
+            H += s_whot[w];
         }
         run = before + inc - tot;
-        if (nhot >= a.n) {
-            H = T;
-        } else {
-            const int wh = nhot / 64;
-            if (wh >= w0 && wh < w0 + per) {
-                int h = run;
-#pragma unroll
-                for (int q = 0; q < PMAX; ++q) {
-                    if (w0 + q < wh) h += __popcll(mw[q]);
-                    else if (w0 + q == wh) h += __popcll(mw[q] & ((1ull << (nhot % 64)) - 1ull));
-                }
-                s_hot = h;
-            }
-            __syncthreads();
-            H = s_hot;
-        }
         C = T - H;
         if (blockIdx.x == 0 && tid == 0) {
             a.out_counts[0] = H;
@@ -172,15 +177,15 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     const float* bgt = part == 0 ? a.bgate[0] : a.bgate[1];
     const int32_t* idx = part == 0 ? a.idx[0] : a.idx[1];
     const int prows = part == 0 ? a.rows[0] : a.rows[1];
+    int32_t* const oidx = part == 0 ? a.out_idx[0] : a.out_idx[1];   // (mask mode) list output
 
     for (int b0 = 0; b0 < a.B; b0 += BT) {
         const int nb = min(BT, a.B - b0);
         if (b0 > 0) {                                  // next token group of x
+            u4 xv[XCH];
+            load_x(xv, b0);
             __syncthreads();
-            const u4* src = reinterpret_cast<const u4*>(a.x + b0 * xrow);
-            u4* dst = reinterpret_cast<u4*>(s_x);
-            const int n16 = (int)(nb * xrow / 16), all16 = (int)(BT * xrow / 16);
-            for (int k = tid; k < all16; k += FT) dst[k] = k < n16 ? src[k] : u4{0u, 0u, 0u, 0u};
+            store_x(xv, b0);
         }
         float acc[BT][NC][EPC];
 #pragma unroll
@@ -200,21 +205,22 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                 int r0 = run;
 #pragma unroll
                 for (int q = 0; q < PMAX; ++q) {
-                    if (q >= per || w0 + q >= words) break;
-                    uint64_t v = s_words[w0 + q];
-                    const int pc = __popcll(v);
-                    if (pc > 0 && r0 < ge && r0 + pc > gb) {
-                        const int skip = max(0, gb - r0);
-                        if (skip > 0) v &= ~((1ull << select_bit(v, skip)) - 1ull);
-                        for (int rank = r0 + skip; v != 0 && rank < ge; ++rank) {
-                            const int id = 64 * (w0 + q) + __builtin_ctzll(v);
-                            v &= v - 1ull;
-                            const int row = part == 0 ? id : id - a.rows[0];
-                            s_row[rank - gb] = (unsigned)row < (unsigned)prows ? row : -1;
-                            if (b0 == 0) a.out_idx[part][rank - hbase] = row;
+                    if (q < per && w0 + q < words) {
+                        uint64_t v = s_words[w0 + q];
+                        const int pc = __popcll(v);
+                        if (pc > 0 && r0 < ge && r0 + pc > gb) {
+                            const int skip = max(0, gb - r0);
+                            if (skip > 0) v &= ~((1ull << select_bit(v, skip)) - 1ull);
+                            for (int rank = r0 + skip; v != 0 && rank < ge; ++rank) {
+                                const int id = 64 * (w0 + q) + __builtin_ctzll(v);
+                                v &= v - 1ull;
+                                const int row = part == 0 ? id : id - a.rows[0];
+                                s_row[rank - gb] = (unsigned)row < (unsigned)prows ? row : -1;
+                                if (b0 == 0) oidx[rank - hbase] = row;
+                            }
                         }
+                        r0 += pc;
                     }
-                    r0 += pc;
                 }
             } else {
                 for (int t = tid; t < len; t += FT) {  // resolve this stage's rows

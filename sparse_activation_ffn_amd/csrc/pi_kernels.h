@@ -491,21 +491,30 @@ struct DownOut {
     int nch;
 };
 
+// floor((a * b + e) / c) for a, b, e >= 0 and c > 0: 32-bit division when the
+// numerator fits (the usual case; a 64-bit division is a long instruction
+// sequence on the GPU), else 64-bit
+__device__ __forceinline__ int muldiv(int a, int b, int e, int c) {
+    const uint64_t p = (uint64_t)(uint32_t)a * (uint32_t)b + (uint32_t)e;
+    if ((p >> 32) == 0) return (int)((uint32_t)p / (uint32_t)c);
+    return (int)(p / (uint32_t)c);
+}
+
 __device__ __forceinline__ void chunk_range(int nch, int H, int C, int k, int& part, int& lo,
                                             int& hi, int& nh) {
     const int T = H + C;
     if (C == 0) nh = nch;
     else if (H == 0) nh = 0;
-    else nh = min(nch - 1, max(1, (int)(((int64_t)nch * H + T / 2) / T)));
+    else nh = min(nch - 1, max(1, muldiv(nch, H, T / 2, T)));
     if (k < nh) {
         part = 0;
-        lo = (int)((int64_t)k * H / nh);
-        hi = (int)((int64_t)(k + 1) * H / nh);
+        lo = muldiv(k, H, 0, nh);
+        hi = muldiv(k + 1, H, 0, nh);
     } else {
         const int kk = k - nh, nc = nch - nh;
         part = 1;
-        lo = (int)((int64_t)kk * C / nc);
-        hi = (int)((int64_t)(kk + 1) * C / nc);
+        lo = muldiv(kk, C, 0, nc);
+        hi = muldiv(kk + 1, C, 0, nc);
     }
 }
 
