@@ -3,6 +3,7 @@
 // template dispatch and the kernel timing hooks.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <algorithm>
 
 #include <cstdarg>
 #include <cstdio>
@@ -81,8 +82,10 @@ bool use_fused(int d, int wt, int xt, int B) {
     const bool pair = (wt == F32 && xt == F32) || (wt != F32 && xt == F16);
     const int nc = fused_nc(d, wt);
     if (!pair || B > FUSED_MAX_BATCH || nc == 0) return false;
-    // x of the token tile, the mask words and the static LDS
-    const size_t lds = (size_t)batch_tile(B) * d * (xt == F32 ? 4 : 2) + 8 * (size_t)MASK_WORDS_MAX + 4096;
+    // x of the token tile and the mask words, or the partial at the end, and
+    // the static LDS
+    const size_t bt = (size_t)batch_tile(B);
+    const size_t lds = std::max(bt * d * (xt == F32 ? 4 : 2) + 8 * (size_t)MASK_WORDS_MAX, bt * d * 4) + 4096;
     if (lds > 160 * 1024) return false;
     if (wt == Q4 && (B > 1 || nc == 4)) return false;
     if (nc == 4 && B > 1) return false;
@@ -293,7 +296,8 @@ template <int WT, int XT, int BT, int ACT, int NC>
 pi_status launch_fused(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
     const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
-    const size_t sh = xbytes + words * 8;            // x, then the mask words
+    const size_t pbytes = (size_t)BT * a.d * 4;       // the partial, staged at the end
+    const size_t sh = std::max(xbytes + words * 8, pbytes);   // x, then the mask words
     auto kern = k_ffn<WT, XT, BT, ACT, NC>;
     TRY(allow_lds(kern, sh));
     TRY(launch(PI_K_FFN, kern, dim3(o.nch), dim3(FT), sh, s, a, o));

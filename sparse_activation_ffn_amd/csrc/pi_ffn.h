@@ -47,15 +47,23 @@ template <> struct Axpy<F16> {
     }
 };
 template <> struct Axpy<Q4> {
-    // one whole block: code byte t -> element t (low nibble), t + 16 (high nibble)
-    __device__ static void run(u4 w, float s, float h, float* acc) {
-        const float hs = h * s;
+    // one whole block: code byte t -> element t (low nibble), t + 16 (high nibble).
+    // hs = h * scale.  acc gets hs * q for the codes q; the caller adds the
+    // -8 hs of the whole block once per block (a running sum of hs), so each
+    // element costs one byte-to-float conversion and one FMA.
+    __device__ static void run(u4 w, float, float hs, float* acc) {
         const unsigned v[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const unsigned byte = (v[t >> 2] >> (8 * (t & 3))) & 0xffu;
-            acc[t] = fmaf(hs, (float)(int)(byte & 15u) - 8.0f, acc[t]);
-            acc[16 + t] = fmaf(hs, (float)(int)(byte >> 4) - 8.0f, acc[16 + t]);
+        for (int m = 0; m < 4; ++m) {
+            unsigned lo = v[m] & 0x0f0f0f0fu, hi = (v[m] >> 4) & 0x0f0f0f0fu;
+            // keep the byte pattern visible, so each byte converts in one
+            // instruction (v_cvt_f32_ubyte0..3) instead of an extract + convert
+            asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                acc[4 * m + b] = fmaf(hs, (float)((lo >> (8 * b)) & 0xffu), acc[4 * m + b]);
+                acc[16 + 4 * m + b] = fmaf(hs, (float)((hi >> (8 * b)) & 0xffu), acc[16 + 4 * m + b]);
+            }
         }
     }
 };
@@ -188,12 +196,15 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
             store_x(xv, b0);
         }
         float acc[BT][NC][EPC];
+        float hsum[BT][NC];                            // Q4_0: running sum of h * scale per chunk
 #pragma unroll
         for (int b = 0; b < BT; ++b)
 #pragma unroll
-            for (int k = 0; k < NC; ++k)
+            for (int k = 0; k < NC; ++k) {
+                hsum[b][k] = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc[b][k][e] = 0.0f;
+            }
 
         for (int s0 = lo; s0 < hi; s0 += FSTAGE) {
             const int len = min(FSTAGE, hi - s0);
@@ -333,8 +344,15 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         }
                         if (r < 0 || b >= nb) hv = 0.0f;
 #pragma unroll
-                        for (int k = 0; k < NC; ++k)
-                            Axpy<WT>::run(R.wd[g][k], WT == Q4 ? half_f(R.sd[g][k]) : 0.f, hv, acc[b][k]);
+                        for (int k = 0; k < NC; ++k) {
+                            if (WT == Q4) {
+                                const float hs = hv * half_f(R.sd[g][k]);
+                                hsum[b][k] += hs;
+                                Axpy<WT>::run(R.wd[g][k], 0.f, hs, acc[b][k]);
+                            } else {
+                                Axpy<WT>::run(R.wd[g][k], 0.f, hv, acc[b][k]);
+                            }
+                        }
                     }
                 }
             };
@@ -348,16 +366,23 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
             }
             __syncthreads();                           // s_red and s_row free for reuse
         }
-        // this workgroup's partial of y for the token group
+        // this workgroup's partial of y for the token group, staged in LDS so the
+        // global stores are contiguous (a thread's columns are a whole chunk
+        // away from its neighbours': direct stores would hit a cache line per lane)
+        __syncthreads();                               // every wave is done with x and the mask words
+        float* s_part = reinterpret_cast<float*>(s_dyn);
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
             if (b < nb) {
-                float* prow = o.partials + ((int64_t)blockIdx.x * a.B + b0 + b) * a.d;
 #pragma unroll
                 for (int k = 0; k < NC; ++k) {
                     const int c = tid + FT * k;
                     if (c < nch) {
-                        f4* dst = reinterpret_cast<f4*>(prow + (int64_t)c * EPC);
+                        if (WT == Q4) {                // the codes' offset of 8: -8 * sum of h * scale
+#pragma unroll
+                            for (int e = 0; e < EPC; ++e) acc[b][k][e] = fmaf(-8.0f, hsum[b][k], acc[b][k][e]);
+                        }
+                        f4* dst = reinterpret_cast<f4*>(s_part + (int64_t)b * a.d + (int64_t)c * EPC);
 #pragma unroll
                         for (int e = 0; e < EPC / 4; ++e)
                             dst[e] = f4{acc[b][k][4 * e], acc[b][k][4 * e + 1], acc[b][k][4 * e + 2],
@@ -365,6 +390,13 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                     }
                 }
             }
+        }
+        __syncthreads();
+        {
+            const int n4 = nb * a.d / 4;               // tokens b0 .. b0 + nb - 1 are contiguous rows
+            f4* dst = reinterpret_cast<f4*>(o.partials + ((int64_t)blockIdx.x * a.B + b0) * a.d);
+            const f4* src = reinterpret_cast<const f4*>(s_part);
+            for (int i = tid; i < n4; i += FT) dst[i] = src[i];
         }
     }
 }
