@@ -297,7 +297,10 @@ pi_status launch_fused(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
     const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
     const size_t pbytes = (size_t)BT * a.d * 4;       // the partial, staged at the end
-    const size_t sh = std::max(xbytes + words * 8, pbytes);   // x, then the mask words
+    size_t sh = std::max(xbytes + words * 8, pbytes);   // x, then the mask words
+#ifdef PI_FFN_LDS_MIN
+    sh = std::max(sh, (size_t)PI_FFN_LDS_MIN);
+#endif
     auto kern = k_ffn<WT, XT, BT, ACT, NC>;
     TRY(allow_lds(kern, sh));
     TRY(launch(PI_K_FFN, kern, dim3(o.nch), dim3(FT), sh, s, a, o));

@@ -227,20 +227,81 @@ template <> struct Down<Q4> {
 };
 
 // ---- reductions ------------------------------------------------------------
+//
+// Cross-lane sums use DPP (data-parallel primitives: a VALU operand read from
+// another lane of the same row of 16 lanes, or broadcast from the last lane of
+// a row), so a 64-lane sum is six dependent VALU adds instead of six LDS
+// permute round trips.  The order of the additions is fixed: results are
+// bit-identical from run to run.
+
+// DPP controls of the GFX9 family (gfx950 included)
+constexpr int DPP_QUAD_1032 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_SHR1 = 0x111;   // row_shr:1 (row_shr:k = 0x110 + k)
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// v + (v of the lane CTRL selects); rows outside ROW_MASK, and lanes whose
+// source lies outside their row, add 0
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float add_dpp(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false);
+    return v + __builtin_bit_cast(float, t);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int add_dpp(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// sum over each row of 16 lanes, in every lane of the row
+template <typename T>
+__device__ __forceinline__ T row_sum16(T v) {
+    v = add_dpp<DPP_QUAD_1032>(v);            // pairs
+    v = add_dpp<DPP_QUAD_2301>(v);            // quads
+    v = add_dpp<DPP_ROW_HALF_MIRROR>(v);      // the other quad of the half row
+    v = add_dpp<DPP_ROW_MIRROR>(v);           // the other half of the row
+    return v;
+}
+
+// sum over the wave, in lane 63 only
+template <typename T>
+__device__ __forceinline__ T wave_sum_last(T v) {
+    v = row_sum16(v);
+    v = add_dpp<DPP_ROW_BCAST15, 0xA>(v);     // rows 1, 3 += rows 0, 2
+    v = add_dpp<DPP_ROW_BCAST31, 0xC>(v);     // rows 2, 3 += rows 0 + 1
+    return v;
+}
 
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-    // sum over aligned groups of W lanes (W a power of two <= 64)
+    // sum over aligned groups of W lanes (W a power of two <= 64), in every lane
+    if constexpr (W == 16) {
+        return row_sum16(v);
+    } else if constexpr (W == WAVE) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_last(v)), WAVE - 1));
+    } else {
 #pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-    return v;
+        for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+        return v;
+    }
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<WAVE>(v); }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return __builtin_amdgcn_readlane(wave_sum_last(v), WAVE - 1);
+}
+
+// inclusive prefix sum over the wave (lane i gets lanes 0..i)
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v = add_dpp<DPP_ROW_SHR1>(v);             // row_shr 1, 2, 4, 8: Hillis-Steele in each row
+    v = add_dpp<DPP_ROW_SHR1 + 1>(v);
+    v = add_dpp<DPP_ROW_SHR1 + 3>(v);
+    v = add_dpp<DPP_ROW_SHR1 + 7>(v);
+    v = add_dpp<DPP_ROW_BCAST15, 0xA>(v);     // rows 1, 3 += last lane of rows 0, 2
+    v = add_dpp<DPP_ROW_BCAST31, 0xC>(v);     // rows 2, 3 += last lane of row 1
     return v;
 }
 

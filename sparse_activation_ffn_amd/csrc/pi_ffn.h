@@ -145,14 +145,9 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                 if (w < words) s_words[w] = v;         // read back by this thread only
             }
         }
-        // exclusive scan of the per-thread totals: shuffles in the wave, then the
+        // exclusive scan of the per-thread totals: DPP in the wave, then the
         // FW wave totals through LDS; the hot counts are only summed
-        int inc = tot;
-#pragma unroll
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const int v = __shfl_up(inc, o, WAVE);
-            if (lane >= o) inc += v;
-        }
+        const int inc = wave_incl_scan(tot);
         hot = wave_sum_int(hot);
         if (lane == WAVE - 1) s_wtot[wv] = inc;
         if (lane == 0) s_whot[wv] = hot;
@@ -311,9 +306,9 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                                                           pg);
                             }
                         }
-                        pu = wave_sum(pu);
-                        if (ACT == REGLU) pg = wave_sum(pg);
-                        if (lane == 0) {
+                        pu = wave_sum_last(pu);
+                        if (ACT == REGLU) pg = wave_sum_last(pg);
+                        if (lane == WAVE - 1) {
                             s_red[slot][wv][g][0][b] = pu;
                             if (ACT == REGLU) s_red[slot][wv][g][NM - 1][b] = pg;
                         }
