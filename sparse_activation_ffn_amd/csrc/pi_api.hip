@@ -85,7 +85,7 @@ bool use_fused(int d, int wt, int xt, int B) {
     // x of the token tile and the mask words, or the partial at the end, and
     // the static LDS
     const size_t bt = (size_t)batch_tile(B);
-    const size_t lds = std::max(bt * d * (xt == F32 ? 4 : 2) + 8 * (size_t)MASK_WORDS_MAX, bt * d * 4) + 4096;
+    const size_t lds = std::max(bt * d * (xt == F32 ? 4 : 2) + 8 * (size_t)FUSED_MASK_WORDS, bt * d * 4) + 4096;
     if (lds > 160 * 1024) return false;
     if (wt == Q4 && (B > 1 || nc == 4)) return false;
     if (nc == 4 && B > 1) return false;
@@ -297,10 +297,7 @@ pi_status launch_fused(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
     const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
     const size_t pbytes = (size_t)BT * a.d * 4;       // the partial, staged at the end
-    size_t sh = std::max(xbytes + words * 8, pbytes);   // x, then the mask words
-#ifdef PI_FFN_LDS_MIN
-    sh = std::max(sh, (size_t)PI_FFN_LDS_MIN);
-#endif
+    const size_t sh = std::max(xbytes + words * 8, pbytes);   // x, then the mask words
     auto kern = k_ffn<WT, XT, BT, ACT, NC>;
     TRY(allow_lds(kern, sh));
     TRY(launch(PI_K_FFN, kern, dim3(o.nch), dim3(FT), sh, s, a, o));
@@ -451,7 +448,7 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
         CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
         Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),
                 const_cast<int32_t*>(counts)};
-        if ((n + 63) / 64 <= MASK_WORDS_MAX) {
+        if ((n + 63) / 64 <= (fused ? FUSED_MASK_WORDS : MASK_WORDS_MAX)) {
             a.mask = mask;                   // compaction fused into k_ffn / k_up
             a.n = n;
             a.out_idx[0] = L.hot;

@@ -24,6 +24,11 @@ namespace pi {
 constexpr int FT = PI_FFN_THREADS;    // threads of the fused kernel (8 waves)
 constexpr int FW = FT / WAVE;
 constexpr int FSTAGE = 256;           // item rows resolved into LDS at a time
+// Largest mask (64-bit words, n <= 65536) that the fused kernel compacts in its
+// prologue (at most two words per thread); a larger mask is compacted by
+// k_compact first and the fused kernel reads the lists.  The bound keeps the
+// prologue's code short: it runs once per launch from a cold instruction cache.
+constexpr int FUSED_MASK_WORDS = 1024;
 
 // acc[0..EPC) += h * (one 16-byte weight chunk, decoded); columns are the
 // chunk's elements in order.
@@ -74,10 +79,15 @@ template <int WT, int XT, int BT, int ACT, int NC>
 __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     constexpr int EPC = Chunk<WT>::EPC;
     constexpr int XB = XT == F32 ? 4 : 2;
-    // rows per group: two register buffers of G rows x NC chunks x (2 or 3 matrices)
-    // plus BT x NC x EPC accumulators must fit in 256 VGPRs
+    // rows per group: the register buffers of the ring (G rows x NC chunks x 2 or
+    // 3 matrices each) plus BT x NC x EPC accumulators must fit in 256 VGPRs.
+    // Two buffers of G2 rows, or, where it holds more rows without spilling,
+    // three buffers of G3 rows (a group's loads are then issued two groups ahead)
     constexpr int G0 = (WT == Q4 ? 4 : 8) / NC / (ACT == REGLU ? 2 : 1) / (BT >= 4 ? 2 : 1);
-    constexpr int G = G0 > 0 ? G0 : 1;
+    constexpr int G2 = G0 > 0 ? G0 : 1;
+    constexpr int G3 = (2 * G2 + 2) / 3;
+    constexpr bool RING3 = BT == 1 && NC <= (WT == Q4 ? 1 : 2) && 3 * G3 > 2 * G2;
+    constexpr int G = RING3 ? G3 : G2;
     constexpr int NM = ACT == REGLU ? 2 : 1;          // dot products per row (up, gate)
     // dynamic LDS: [x for BT tokens] [mask words]
     extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
@@ -96,7 +106,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     // Prologue, one memory round trip: this thread's share of x and its run of
     // mask words are loaded before anything waits on either (x first, so the
     // wait at the join after the conditional mask loads covers both).
-    constexpr int PMAX = (MASK_WORDS_MAX + FT - 1) / FT;
+    constexpr int PMAX = (FUSED_MASK_WORDS + FT - 1) / FT;
     constexpr int XCH = BT * NC * EPC * XB / 16;       // 16-byte x pieces per thread (d <= NC FT EPC)
     const int words = a.mask ? (a.n + 63) / 64 : 0;
     const int per = (words + FT - 1) / FT;             // mask words per thread (<= PMAX)
@@ -125,6 +135,11 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
         mw[q] = 0;
         if (q < per) mw[q] = a.mask[min(w0 + q, words - 1)];
     }
+    // the weight and bias pointers and the output descriptor sit in
+    // kernel-argument cache lines that nothing above reads: fetch them now,
+    // while x and the mask are in flight, rather than as scalar-cache misses
+    // after the scan
+    asm volatile("" ::"s"(a.up[0]), "s"(a.bup[0]), "s"(o.partials), "s"(o.nch));
     store_x(xv0, 0);
     int H, C;
     int run = 0;                                       // rank of this thread's first set bit
@@ -351,13 +366,32 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                     }
                 }
             };
-            Regs A, Bn;
-            load_group(A, 0);
-            for (int g0 = 0; g0 < len; g0 += 2 * G) {
-                if (g0 + G < len) load_group(Bn, g0 + G);
-                process_group(A, 0);
-                if (g0 + 2 * G < len) load_group(A, g0 + 2 * G);
-                if (g0 + G < len) process_group(Bn, 1);
+            // groups go round a ring of register buffers: a buffer is refilled
+            // with the group after next (two-buffer ring) or the group three
+            // ahead (three-buffer ring) as soon as it is consumed; reduction
+            // slots alternate with the group index
+            if constexpr (RING3) {
+                Regs R0, R1, R2;
+                load_group(R0, 0);
+                if (G < len) load_group(R1, G);
+                for (int g0 = 0; g0 < len; g0 += 3 * G) {
+                    const int k = g0 / G;              // index of the group in R0
+                    if (g0 + 2 * G < len) load_group(R2, g0 + 2 * G);
+                    process_group(R0, k & 1);
+                    if (g0 + 3 * G < len) load_group(R0, g0 + 3 * G);
+                    if (g0 + G < len) process_group(R1, (k + 1) & 1);
+                    if (g0 + 4 * G < len) load_group(R1, g0 + 4 * G);
+                    if (g0 + 2 * G < len) process_group(R2, k & 1);
+                }
+            } else {
+                Regs A, Bn;
+                load_group(A, 0);
+                for (int g0 = 0; g0 < len; g0 += 2 * G) {
+                    if (g0 + G < len) load_group(Bn, g0 + G);
+                    process_group(A, 0);
+                    if (g0 + 2 * G < len) load_group(A, g0 + 2 * G);
+                    if (g0 + G < len) process_group(Bn, 1);
+                }
             }
             __syncthreads();                           // s_red and s_row free for reuse
         }
