@@ -230,6 +230,9 @@ def main():
     ap.add_argument("--instances", type=int, default=INSTANCES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cold-host", action="store_true",
+                    help="place the cold partition's weight rows in pinned host memory "
+                         "(capacity tier), read by the kernels over the host link")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of a captured HIP graph")
     args = ap.parse_args()
@@ -264,6 +267,10 @@ def main():
         perm_np = perm.cpu().numpy()
         del X
     layers = [base] + [base.clone() for _ in range(args.instances - 1)]
+    if args.cold_host:
+        log("[bench] placing the cold partition in pinned host memory ...")
+        for ly in layers:
+            ly.place_cold_on_host()
     descs = [(ly.predictor(), ly.parts()) for ly in layers]
     buf = StepBuffers(base, B, dev)
     xs = [torch.from_numpy(S.make_x(wl, 0, s, B)).to(dev) for s in range(W + K)]
@@ -378,6 +385,9 @@ def main():
         "achieved_gbps_touched": round(gbps_touched, 1),
         "frac_of_peak_touched": round(gbps_touched / PEAK_HBM_GBPS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items() if kern_ms[k][1] > 0},
+        "cold_tier": "host" if args.cold_host and n_hot < wl.n else "hbm",
+        "cold_bytes_per_step": round(float(np.mean([a - h for a, h in zip(active, hot_active)]))
+                                     * ((3 if wl.act == "reglu" else 2) * wrow_bytes(wl) + 4)),
         "kernel_bytes": {k: round(kb_mean[k]) for k in kern_us if kern_ms[k][1] > 0},
         "roofline": roofline, "dense_ffn": dense, "cpu_baseline": cpu,
     }

@@ -71,8 +71,36 @@ class DeviceLayer:
 
     def parts(self):
         hot = self.part(0, self.n_hot)
-        cold = self.part(self.n_hot, self.n) if self.n_hot < self.n else None
+        cold = None
+        if self.n_hot < self.n:
+            ch = getattr(self, "cold_host", None)
+            if ch is None:
+                cold = self.part(self.n_hot, self.n)
+            else:
+                s = lambda t: pb.row_slice(t, self.n_hot, self.n)  # noqa: E731
+                cold = pb.make_part(self.d, ch["W_up"], ch["W_downT"], self.act, ch["W_gate"],
+                                    s(self.b_up), s(self.b_gate), q4=self.q4)
         return hot, cold
+
+    # ---- capacity tiers ---------------------------------------------------------
+    def place_cold_on_host(self):
+        """Capacity-tiered placement (CSDN article, hybrid-design section: the hot
+        neurons stay on the GPU, the cold ones live in host memory): the weight rows
+        of the cold partition are copied into pinned host memory, which the GPU reads
+        directly over the host link; the hot partition, the predictor and the biases
+        stay in device memory.  parts() then describes the cold partition at its
+        host addresses; the kernels are the same."""
+        if self.n_hot >= self.n:
+            return
+
+        def host(t):
+            if t is None:
+                return None
+            h = torch.empty(t[self.n_hot:].shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(t[self.n_hot:])
+            return h
+        self.cold_host = {"W_up": host(self.W_up), "W_gate": host(self.W_gate),
+                          "W_downT": host(self.W_downT)}
 
     # ---- offline: profiling and neuron index ----------------------------------
     def profile_counts(self, X: torch.Tensor) -> torch.Tensor:

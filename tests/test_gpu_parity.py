@@ -262,6 +262,27 @@ def test_wide_mask_compacted_before_fused_kernel():
         log(f"  wide mask step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
 
 
+def test_cold_partition_in_host_memory():
+    """Cold partition's weight rows in pinned host memory, read by the same kernels
+    over the host link: bit-identical to the all-device layer, and oracle parity."""
+    wl = SMALL["opt30b-fp16"]
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    Lh, n_hot = index_layer(L, dl, 256)
+    buf = StepBuffers(dl, 1, DEV)
+    xs = [S.make_x(wl, 0, step, 1) for step in range(3)]
+    ref = [run_step(dl, buf, x) for x in xs]
+    dl.place_cold_on_host()
+    hot, cold = dl.parts()
+    assert cold is not None and not dl.cold_host["W_up"].is_cuda
+    for step, x in enumerate(xs):
+        out = run_step(dl, buf, x, fused=(step != 1))
+        for k in ("y", "y_hot", "y_cold", "hot", "cold"):
+            assert np.array_equal(out[k], ref[step][k]), k
+        e, namb, na = check_step(Lh, n_hot, x, out)
+        log(f"  cold on host, step {step}: active {na}, err {e:.2e}")
+
+
 def test_deterministic_reruns(small_f16):
     wl, L = small_f16
     dl = DeviceLayer.upload(L, DEV, n_hot=200)
