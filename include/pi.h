@@ -219,6 +219,19 @@ pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budge
                                 void* stream);
 
 /*
+ * Online activation statistics (hada.io README summary: "recent updates"
+ * lists online FFN splitting, and the FAQ rebuilds the GPU index on demand):
+ * counts[i] += bit i of mask, for i < n (mask as written by pi_predict, in
+ * the current slot order).  Accumulated over decode steps, counts feed
+ * pi_build_neuron_index again, so the hot partition follows the predicted
+ * activations the layer actually sees.  mask [ceil(n/64)] uint64 device,
+ * 8-byte aligned; counts [n] uint32 device, 4-byte aligned, updated in place
+ * (each counter by one thread: no atomics, exact).  Errors (NULL pointers,
+ * misalignment, n < 1) enqueue nothing.
+ */
+pi_status pi_accumulate_mask(const uint64_t* mask, int32_t n, uint32_t* counts, void* stream);
+
+/*
  * Applies a neuron index to one per-neuron tensor: dst row s = src row
  * perm[s], rows of row_bytes bytes (row_bytes % 4 == 0), s < rows.  src and
  * dst must not overlap.
@@ -245,7 +258,8 @@ enum {
     PI_K_COPY = 8,
     PI_K_REDUCE = 9,      /* partials of y -> y_hot, y_cold, y (fused merge) */
     PI_K_FFN = 10,        /* fused compaction + up/gate + activation + down (batch <= 4) */
-    PI_K_COUNT = 11
+    PI_K_ACCUMULATE = 11, /* online activation counts from a mask */
+    PI_K_COUNT = 12
 };
 
 /*

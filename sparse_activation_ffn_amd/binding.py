@@ -21,12 +21,13 @@ PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
 PI_RELU, PI_REGLU = 0, 1
 PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
- PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_COUNT) = range(12)
+ PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_COUNT) = range(13)
 
 # every symbol include/pi.h declares
 EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_active",
            "pi_sparse_ffn", "pi_sparse_ffn_split", "pi_merge", "pi_dense_ffn",
-           "pi_profile_counts", "pi_build_neuron_index", "pi_permute_rows", "pi_copy",
+           "pi_profile_counts", "pi_build_neuron_index", "pi_accumulate_mask", "pi_permute_rows",
+           "pi_copy",
            "pi_kernel_timer_start", "pi_kernel_timer_stop", "pi_kernel_name", "pi_status_string",
            "pi_last_error")
 
@@ -78,6 +79,7 @@ def lib() -> C.CDLL:
         "pi_dense_ffn": ([P, P, I32, I32, P, P, SZ, P], I32),
         "pi_profile_counts": ([P, P, I32, I32, P, P], I32),
         "pi_build_neuron_index": ([P, I32, I64, I64, P, P, P], I32),
+        "pi_accumulate_mask": ([P, I32, P, P], I32),
         "pi_permute_rows": ([P, P, P, I32, I64, P], I32),
         "pi_copy": ([P, P, I64, P], I32),
         "pi_kernel_timer_start": ([I32, I32], I32),
@@ -188,6 +190,10 @@ def pi_build_neuron_index(counts, budget_bytes: int, bytes_per_neuron: int, perm
                                        int(bytes_per_neuron), ptr(perm), C.byref(n_hot),
                                        stream_handle(stream)))
     return int(n_hot.value)
+
+
+def pi_accumulate_mask(mask, n: int, counts, stream=None):
+    _check(lib().pi_accumulate_mask(ptr(mask), n, ptr(counts), stream_handle(stream)))
 
 
 def pi_permute_rows(src, dst, perm, rows: int, row_bytes: int, stream=None):

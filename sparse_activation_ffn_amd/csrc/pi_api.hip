@@ -505,7 +505,7 @@ const char* pi_last_error(void) { return g_err; }
 const char* pi_kernel_name(int32_t kid) {
     static const char* names[PI_K_COUNT] = {"k_pred_l1", "k_pred_l2", "k_compact", "k_up", "k_down",
                                             "k_merge", "k_profile", "k_index", "k_copy", "k_reduce",
-                                            "k_ffn"};
+                                            "k_ffn", "k_accumulate_mask"};
     return (kid >= 0 && kid < PI_K_COUNT) ? names[kid] : "?";
 }
 
@@ -680,6 +680,14 @@ pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budge
     if (n == 0) return PI_OK;
     return launch(PI_K_INDEX, k_index, dim3((n + THREADS - 1) / THREADS), dim3(THREADS), 0,
                   (hipStream_t)stream, counts, n, perm);
+}
+
+pi_status pi_accumulate_mask(const uint64_t* mask, int32_t n, uint32_t* counts, void* stream) {
+    CHECK(n >= 1 && n <= (1 << 24), PI_ERR_SHAPE, "n must be in 1..2^24");
+    CHECK(mask && counts, PI_ERR_ARG, "mask and counts required");
+    CHECK(aligned(mask, 8) && aligned(counts, 4), PI_ERR_ALIGN, "misaligned mask or counts");
+    return launch(PI_K_ACCUMULATE, k_accumulate_mask, dim3((n + THREADS - 1) / THREADS), dim3(THREADS),
+                  0, (hipStream_t)stream, mask, n, counts);
 }
 
 pi_status pi_permute_rows(const void* src, void* dst, const int32_t* perm, int32_t rows,

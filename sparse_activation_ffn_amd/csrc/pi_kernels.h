@@ -698,6 +698,14 @@ __global__ __launch_bounds__(THREADS) void k_profile(const uint8_t* __restrict__
 // Neuron index: rank_i = #{j : c_j > c_i} + #{j < i : c_j == c_i}; perm[rank_i] = i.
 // Exact, deterministic, O(n^2) compares over LDS tiles of the counts.
 // ===========================================================================
+// Online activation counts: counter i owned by thread i, so no atomics and the
+// result is exact and independent of scheduling.
+__global__ __launch_bounds__(THREADS) void k_accumulate_mask(const uint64_t* __restrict__ mask, int n,
+                                                             uint32_t* __restrict__ counts) {
+    const int i = blockIdx.x * THREADS + threadIdx.x;
+    if (i < n) counts[i] += (uint32_t)((mask[i >> 6] >> (i & 63)) & 1ull);
+}
+
 __global__ __launch_bounds__(THREADS) void k_index(const uint32_t* __restrict__ counts, int n,
                                                    int32_t* __restrict__ perm) {
     constexpr int TILE = 4096;

@@ -82,6 +82,26 @@ class DeviceLayer:
                                     s(self.b_up), s(self.b_gate), q4=self.q4)
         return hot, cold
 
+    # ---- online index maintenance -------------------------------------------------
+    def accumulate(self, mask: torch.Tensor, counts: torch.Tensor):
+        """counts[i] += predicted bit i of this step's mask (current slot order)."""
+        pb.pi_accumulate_mask(mask, self.n, counts)
+
+    def reindex(self, counts: torch.Tensor, budget_bytes: int, bytes_per_neuron: int):
+        """Online FFN splitting (hada.io README summary, recent updates; the FAQ
+        rebuilds the GPU index): a new neuron index from counts gathered during
+        decode, applied to the already-indexed layer.  counts is permuted with the
+        rows, so it keeps describing the slots.  Returns (perm, n_hot), perm mapping
+        each new slot to its slot before this call."""
+        perm, n_hot = self.build_index(counts, budget_bytes, bytes_per_neuron)
+        self.apply_index(perm, n_hot)
+        moved = torch.empty_like(counts)
+        pb.pi_permute_rows(counts, moved, perm, self.n, 4)
+        counts.copy_(moved)
+        if getattr(self, "cold_host", None) is not None:
+            self.place_cold_on_host()
+        return perm, n_hot
+
     # ---- capacity tiers ---------------------------------------------------------
     def place_cold_on_host(self):
         """Capacity-tiered placement (CSDN article, hybrid-design section: the hot

@@ -283,6 +283,40 @@ def test_cold_partition_in_host_memory():
         log(f"  cold on host, step {step}: active {na}, err {e:.2e}")
 
 
+def test_online_counts_and_reindex():
+    """Predicted activations counted on the device during decode (exact integer
+    sums of the masks), then a new neuron index from them applied to the indexed
+    layer: index equal to the oracle's for the same counts, and step parity after."""
+    wl = SMALL["opt30b-fp16"]
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    Lh, n_hot = index_layer(L, dl, 256)
+    buf = StepBuffers(dl, 1, DEV)
+    counts = torch.zeros(wl.n, dtype=torch.int32, device=DEV)
+    want = np.zeros(wl.n, dtype=np.int64)
+    for step in range(6):
+        x = S.make_x(wl, 0, 100 + step, 1)
+        out = run_step(dl, buf, x, fused=(step % 2 == 0))
+        check_step(Lh, n_hot, x, out)
+        dl.accumulate(buf.mask, counts)
+        want += mask_bits(out["mask"], wl.n)[0]
+    torch.cuda.synchronize()
+    got = _np(counts).astype(np.uint32)
+    assert np.array_equal(got.astype(np.int64), want)
+    bpn, budget = S.bytes_per_neuron(wl), S.budget_bytes(wl)
+    perm, n_hot2 = dl.reindex(counts, budget, bpn)
+    torch.cuda.synchronize()
+    perm_o, n_hot_o = O.build_neuron_index(got, budget, bpn)
+    assert n_hot2 == n_hot_o and np.array_equal(_np(perm), perm_o)
+    assert np.array_equal(_np(counts).astype(np.uint32), got[perm_o])
+    Lh2 = permute_layer(Lh, perm_o)
+    buf2 = StepBuffers(dl, 1, DEV)
+    for step in range(2):
+        x = S.make_x(wl, 0, 200 + step, 1)
+        e, namb, na = check_step(Lh2, n_hot2, x, run_step(dl, buf2, x))
+        log(f"  after online reindex, step {step}: active {na}, err {e:.2e}")
+
+
 def test_deterministic_reruns(small_f16):
     wl, L = small_f16
     dl = DeviceLayer.upload(L, DEV, n_hot=200)
