@@ -28,6 +28,9 @@
  *  - Sparse FFN over a list L, per token b:
  *      ReLU : h_i = max(0, W_up[i].x_b + b_up[i])
  *      ReGLU: h_i = max(0, W_gate[i].x_b + b_gate[i]) * (W_up[i].x_b + b_up[i])
+ *      Squared ReLU: h_i = max(0, W_up[i].x_b + b_up[i])^2 (the third activation
+ *             the hada.io README summary lists as supported, next to ReLU and
+ *             ReGLU; deciding pre-activation as for ReLU)
  *      y_b  = sum over i in L (ascending) of h_i * W_downT[i][:]
  *    Missing biases are zero.  No down-projection bias.
  *  - Hot/cold: hot = ids < n_hot of the permuted layer, cold = the rest;
@@ -51,7 +54,7 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_Q4_0 = 2 };
-enum { OR_RELU = 0, OR_REGLU = 1 };
+enum { OR_RELU = 0, OR_REGLU = 1, OR_SQRELU = 2 };
 enum { OR_OK = 0, OR_BAD = 1 };
 
 /* ---- storage decoding ------------------------------------------------ */
@@ -237,6 +240,9 @@ int or_sparse_ffn(const or_part* p, const void* x, int xdtype, int64_t B, const 
             double h;
             if (p->act == OR_RELU) {
                 h = up > 0.0 ? up : 0.0;
+            } else if (p->act == OR_SQRELU) {
+                const double r = up > 0.0 ? up : 0.0;
+                h = r * r;
             } else {
                 or_load_row(p->W_gate, p->wdtype, d, i, row);
                 double g = or_dot(row, xb, d) + (p->b_gate ? (double)p->b_gate[i] : 0.0);

@@ -22,9 +22,9 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 F32, F16, Q4_0 = 0, 1, 2
-RELU, REGLU = 0, 1
+RELU, REGLU, SQRELU = 0, 1, 2
 DT = {"f32": F32, "f16": F16, "q4_0": Q4_0}
-ACT = {"relu": RELU, "reglu": REGLU}
+ACT = {"relu": RELU, "reglu": REGLU, "sqrelu": SQRELU}
 
 
 def build(force: bool = False) -> str:

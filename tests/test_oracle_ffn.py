@@ -10,6 +10,8 @@ design: the partitions' partial results merge into the layer output):
 - brute force over all 2^n masks on tiny layers: y(M) == y(M & firing);
 - rows outside the list may be NaN-poisoned without changing y;
 - ReGLU with W_up row = e_k and x_k = 1 reduces to the ReLU FFN on the gate;
+- squared ReLU equals ReGLU with the gate set to the up projection
+  (max(0, a)^2 == max(0, a) * a), and an integer fixture gives h = a^2;
 - Q4_0: the FFN on Q4_0 weights equals the FFN on the same weights decoded
   to float32 (the decode is exact);
 - split + merge equals the unsplit layer bit for bit on integer fixtures,
@@ -39,59 +41,61 @@ def _layer(rng, n, d, act="relu", dt=np.float32, integer=False, bias=True):
         W_gate = (rng.standard_normal((n, d)) / np.sqrt(d)).astype(dt)
         W_downT = (rng.standard_normal((n, d)) / np.sqrt(n)).astype(dt)
         b = (rng.standard_normal(n) * 0.5).astype(np.float32)
-    if act == "relu":
-        return O.Part(d, W_up, W_downT, act="relu", b_up=b if bias else None)
+    if act in ("relu", "sqrelu"):
+        return O.Part(d, W_up, W_downT, act=act, b_up=b if bias else None)
     return O.Part(d, W_up, W_downT, act="reglu", W_gate=W_gate, b_gate=b if bias else None)
 
 
-def _np_ffn(part, x):
+def _np_ffn(part, x, act="relu"):
     W_up, W_gate, b_up, b_gate, W_downT = [None if a is None else a.astype(np.float64)
                                            for a in part.arrays]
     xx = x.astype(np.float64)
     up = xx @ W_up.T + (0 if b_up is None else b_up)
-    if W_gate is None:
+    if act == "sqrelu":
+        h = np.maximum(up, 0) ** 2
+    elif W_gate is None:
         h = np.maximum(up, 0)
     else:
         h = np.maximum(xx @ W_gate.T + (0 if b_gate is None else b_gate), 0) * up
     return h @ W_downT, up, h
 
 
-def _firing(part, x):
-    _, up, h = _np_ffn(part, x)
+def _firing(part, x, act="relu"):
+    _, up, h = _np_ffn(part, x, act)
     return np.flatnonzero((h != 0).any(axis=0)).astype(np.int32)
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "reglu", "sqrelu"])
 @pytest.mark.parametrize("dt", [np.float32, np.float16])
 def test_dense_matches_numpy(act, dt):
     rng = np.random.default_rng(11)
     part = _layer(rng, 150, 64, act, dt)
     x = rng.standard_normal((3, 64)).astype(dt)
-    ref, _, _ = _np_ffn(part, x)
+    ref, _, _ = _np_ffn(part, x, act)
     np.testing.assert_allclose(O.dense_ffn(part, x), ref, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "reglu", "sqrelu"])
 def test_sparse_equals_dense_on_full_true_and_superset(act):
     rng = np.random.default_rng(5)
     part = _layer(rng, 300, 64, act)
     x = rng.standard_normal((1, 64)).astype(np.float32)
     dense = O.dense_ffn(part, x)
     assert np.array_equal(O.sparse_ffn(part, x, np.arange(300)), dense)
-    fire = _firing(part, x)
+    fire = _firing(part, x, act)
     assert 0 < fire.size < 300
     assert np.array_equal(O.sparse_ffn(part, x, fire), dense)
     extra = np.union1d(fire, rng.choice(300, 40, replace=False)).astype(np.int32)
     assert np.array_equal(O.sparse_ffn(part, x, extra), dense)
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "reglu", "sqrelu"])
 def test_brute_force_all_masks(act):
     rng = np.random.default_rng(9 + len(act))
     n, d = 10, 16
     part = _layer(rng, n, d, act)
     x = rng.standard_normal((1, d)).astype(np.float32)
-    fire = set(_firing(part, x).tolist())
+    fire = set(_firing(part, x, act).tolist())
     assert 0 < len(fire) < n
     for bits in itertools.product([0, 1], repeat=n):
         M = [i for i in range(n) if bits[i]]
@@ -128,6 +132,32 @@ def test_reglu_reduces_to_relu_on_gate():
     reglu = O.Part(d, W_up, W_downT, act="reglu", W_gate=W_gate, b_gate=b_gate)
     relu = O.Part(d, W_gate, W_downT, act="relu", b_up=b_gate)
     assert np.array_equal(O.dense_ffn(reglu, x), O.dense_ffn(relu, x))
+
+
+def test_squared_relu_is_reglu_with_gate_equal_to_up():
+    """max(0, a)^2 == max(0, a) * a: the squared-ReLU FFN equals the ReGLU FFN of the
+    same layer with W_gate := W_up and b_gate := b_up, bit for bit (the same dot
+    product in the same order on both branches)."""
+    rng = np.random.default_rng(23)
+    n, d = 120, 64
+    sq = _layer(rng, n, d, "sqrelu")
+    W_up, _, b_up, _, W_downT = sq.arrays
+    gl = O.Part(d, W_up, W_downT, act="reglu", W_gate=W_up, b_up=b_up, b_gate=b_up)
+    x = rng.standard_normal((2, d)).astype(np.float32)
+    assert np.array_equal(O.dense_ffn(sq, x), O.dense_ffn(gl, x))
+    idx = np.sort(rng.choice(n, 40, replace=False)).astype(np.int32)
+    assert np.array_equal(O.sparse_ffn(sq, x, idx), O.sparse_ffn(gl, x, idx))
+
+
+def test_squared_relu_integer_fixture():
+    """Integer fixture: a = W_up.x + b exactly, h = a^2 for a > 0, 0 otherwise."""
+    d = 4
+    W_up = np.array([[1, 2, 0, 0], [0, -1, 0, 0], [3, 0, 0, 1]], dtype=np.float32)
+    b_up = np.array([0, 0, -5], dtype=np.float32)
+    W_downT = np.eye(3, d, dtype=np.float32)          # y[i] = h_i for i < 3
+    part = O.Part(d, W_up, W_downT, act="sqrelu", b_up=b_up)
+    x = np.array([[1, 1, 7, 4]], dtype=np.float32)     # a = 3, -1, 2 -> h = 9, 0, 4
+    assert O.dense_ffn(part, x).tolist() == [[9.0, 0.0, 4.0, 0.0]]
 
 
 def test_q4_0_ffn_equals_decoded_fp32_ffn():

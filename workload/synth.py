@@ -65,7 +65,7 @@ P_CLIP = 0.99
 T_PERM, T_WUP, T_WGATE, T_WDOWN, T_P1, T_P2, T_X, T_PROF, T_QCODE, T_QSCALE = range(10)
 
 F32, F16, Q4_0 = "f32", "f16", "q4_0"
-RELU, REGLU = "relu", "reglu"
+RELU, REGLU, SQRELU = "relu", "reglu", "sqrelu"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -79,7 +79,7 @@ class Workload:
     wdtype: str               # FFN weight storage: f32 / f16 / q4_0
     pdtype: str               # predictor weight storage: f32 / f16
     xdtype: str               # input storage: f32 / f16
-    act: str                  # relu / reglu
+    act: str                  # relu / reglu / sqrelu (squared ReLU: deciding row W_up, as ReLU)
     mean: float               # mean firing probability
     batches: tuple = (1,)
     steps: int = 64
@@ -262,10 +262,10 @@ def make_layer(wl: Workload, layer: int = 0, predictor_bias: bool = True, thread
         if wl.act == REGLU:
             W_gate = _normal_matrix(wl, layer, T_WGATE, n, d, 1.0 / math.sqrt(d), wl.wdtype, threads)
             gate_norm = _row_norms(W_gate)
-    if wl.act == RELU:
-        b_up = (up_norm * z).astype(np.float32)
-    else:
+    if wl.act == REGLU:
         b_gate = (gate_norm * z).astype(np.float32)
+    else:
+        b_up = (up_norm * z).astype(np.float32)
     P1t = _normal_matrix(wl, layer, T_P1, r, d, 1.0 / math.sqrt(d), wl.pdtype, threads)
     P2t = _normal_matrix(wl, layer, T_P2, n, r, 1.0 / math.sqrt(r), wl.pdtype, threads)
     b2 = (z / math.sqrt(2.0)).astype(np.float32) if predictor_bias else np.zeros(n, np.float32)
