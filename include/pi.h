@@ -60,8 +60,9 @@ enum {
 
 /* element storage types */
 enum { PI_F32 = 0, PI_F16 = 1, PI_Q4_0 = 2 };
-/* FFN activations (hada.io README summary: ReLU and ReGLU models) */
-enum { PI_RELU = 0, PI_REGLU = 1 };
+/* FFN activations (hada.io README summary, supported models: ReLU, ReGLU and
+ * squared-ReLU models) */
+enum { PI_RELU = 0, PI_REGLU = 1, PI_SQRELU = 2 };
 
 /* Largest batch a call accepts. */
 #define PI_MAX_BATCH 64
@@ -97,9 +98,9 @@ typedef struct pi_ffn_part {
     int32_t d;            /* model width: d % 64 == 0 (d % 256 == 0 for Q4_0) */
     int32_t rows;         /* neurons in this partition, >= 0 */
     int32_t wdtype;       /* PI_F32, PI_F16 or PI_Q4_0 (all three matrices) */
-    int32_t act;          /* PI_RELU or PI_REGLU */
+    int32_t act;          /* PI_RELU, PI_REGLU or PI_SQRELU (h = max(0, W_up.x + b_up)^2) */
     const void* W_up;     /* [rows][d] */
-    const void* W_gate;   /* [rows][d], required for PI_REGLU, ignored for PI_RELU */
+    const void* W_gate;   /* [rows][d], required for PI_REGLU, ignored otherwise */
     const float* b_up;    /* [rows] or NULL */
     const float* b_gate;  /* [rows] or NULL */
     const void* W_downT;  /* [rows][d] */

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libpi.so")
 PI_OK, PI_ERR_ARG, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_DTYPE, PI_ERR_WORKSPACE, PI_ERR_BUDGET, \
     PI_ERR_HIP = range(8)
 PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
-PI_RELU, PI_REGLU = 0, 1
+PI_RELU, PI_REGLU, PI_SQRELU = 0, 1, 2
 PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
  PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_COUNT) = range(13)

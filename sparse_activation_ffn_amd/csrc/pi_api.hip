@@ -162,16 +162,17 @@ pi_status check_part(const pi_ffn_part* p, const char* name, bool allow_empty) {
     CHECK(p, PI_ERR_ARG, "%s: NULL partition", name);
     CHECK(p->wdtype == PI_F32 || p->wdtype == PI_F16 || p->wdtype == PI_Q4_0, PI_ERR_DTYPE,
           "%s: wdtype must be PI_F32, PI_F16 or PI_Q4_0", name);
-    CHECK(p->act == PI_RELU || p->act == PI_REGLU, PI_ERR_ARG, "%s: act must be PI_RELU or PI_REGLU", name);
+    CHECK(p->act == PI_RELU || p->act == PI_REGLU || p->act == PI_SQRELU, PI_ERR_ARG,
+          "%s: act must be PI_RELU, PI_REGLU or PI_SQRELU", name);
     CHECK(p->d > 0 && p->d % 64 == 0, PI_ERR_SHAPE, "%s: d must be a positive multiple of 64", name);
     CHECK(p->wdtype != PI_Q4_0 || p->d % 256 == 0, PI_ERR_SHAPE, "%s: Q4_0 rows need d %% 256 == 0", name);
     CHECK(p->d <= down_cols(p->wdtype) * MAX_SLICES, PI_ERR_SHAPE, "%s: d too large", name);
     CHECK(p->rows >= 0 && (allow_empty || p->rows > 0), PI_ERR_SHAPE, "%s: bad row count", name);
     if (p->rows == 0) return PI_OK;
     CHECK(p->W_up && p->W_downT, PI_ERR_ARG, "%s: W_up and W_downT are required", name);
-    CHECK(p->act == PI_RELU || p->W_gate, PI_ERR_ARG, "%s: ReGLU needs W_gate", name);
+    CHECK(p->act != PI_REGLU || p->W_gate, PI_ERR_ARG, "%s: ReGLU needs W_gate", name);
     CHECK(aligned(p->W_up, 16) && aligned(p->W_downT, 16) &&
-              (p->act == PI_RELU || aligned(p->W_gate, 16)),
+              (p->act != PI_REGLU || aligned(p->W_gate, 16)),
           PI_ERR_ALIGN, "%s: weights must be 16-byte aligned", name);
     CHECK(aligned(p->b_up, 4) && aligned(p->b_gate, 4), PI_ERR_ALIGN, "%s: biases must be 4-byte aligned", name);
     return PI_OK;
@@ -274,8 +275,8 @@ pi_status launch_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
 
 template <int WT, int XT, int BT>
 pi_status ffn_act(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
-    pi_status st = act == PI_RELU ? launch_up<WT, XT, BT, RELU>(a, rows_cap, s)
-                                  : launch_up<WT, XT, BT, REGLU>(a, rows_cap, s);
+    pi_status st = act != PI_REGLU ? launch_up<WT, XT, BT, RELU>(a, rows_cap, s)
+                                   : launch_up<WT, XT, BT, REGLU>(a, rows_cap, s);
     if (st != PI_OK) return st;
     return launch_down<WT, BT>(a, o, s);
 }
@@ -317,8 +318,8 @@ pi_status fused_nc_dispatch(const FfnArgs& a, const DownOut& o, hipStream_t s) {
 
 template <int WT, int XT, int BT>
 pi_status fused_act(const FfnArgs& a, const DownOut& o, int act, hipStream_t s) {
-    return act == PI_RELU ? fused_nc_dispatch<WT, XT, BT, RELU>(a, o, s)
-                          : fused_nc_dispatch<WT, XT, BT, REGLU>(a, o, s);
+    return act != PI_REGLU ? fused_nc_dispatch<WT, XT, BT, RELU>(a, o, s)
+                           : fused_nc_dispatch<WT, XT, BT, REGLU>(a, o, s);
 }
 
 template <int WT, int XT>
@@ -372,7 +373,7 @@ pi_status mfma_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
 
 template <int WT>
 pi_status run_mfma_wt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
-    if (act == PI_RELU) TRY((mfma_up_mt<WT, RELU>(a, rows_cap, s)));
+    if (act != PI_REGLU) TRY((mfma_up_mt<WT, RELU>(a, rows_cap, s)));
     else TRY((mfma_up_mt<WT, REGLU>(a, rows_cap, s)));
     const bool lists = a.idx[0] || a.idx[1];          // else dense rows
     switch (mfma_mt(a.B) * 2 + (lists ? 1 : 0)) {
@@ -444,6 +445,7 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.nparts = has_cold ? 2 : 1;
     a.rows[0] = hot->rows;
     a.rows[1] = has_cold ? cold->rows : 0;
+    a.square = hot->act == PI_SQRELU;              // squared ReLU: the ReLU kernels, h squared
     if (mask) {
         CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
         Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),

@@ -347,7 +347,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         up += bu;
                         float hv;
                         if (ACT == RELU) {
-                            hv = up > 0.0f ? up : 0.0f;
+                            hv = up > 0.0f ? (a.square ? up * up : up) : 0.0f;
                         } else {
                             gt += bg;
                             hv = (gt > 0.0f ? gt : 0.0f) * up;

@@ -28,7 +28,7 @@ class DeviceLayer:
     def __init__(self, d, n, r, act, wdtype_q4, W_up, W_gate, W_downT, b_up, b_gate, P1t, P2t,
                  b2, threshold=0.0, n_hot=None):
         self.d, self.n, self.r = d, n, r
-        self.act = pb.PI_REGLU if act in ("reglu", pb.PI_REGLU) else pb.PI_RELU
+        self.act = {"relu": pb.PI_RELU, "reglu": pb.PI_REGLU, "sqrelu": pb.PI_SQRELU}.get(act, act)
         self.q4 = wdtype_q4
         self.W_up, self.W_gate, self.W_downT = W_up, W_gate, W_downT
         self.b_up, self.b_gate = b_up, b_gate

@@ -142,6 +142,33 @@ def test_small_parity(name, B):
         log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
 
 
+SQRELU_SMALL = {
+    "f16": S.WORKLOADS["opt30b-fp16"].scaled(d=576, n=2085, r=64, act="sqrelu"),
+    "f32": S.WORKLOADS["opt-fp32"].scaled(d=320, n=1000, r=32, act="sqrelu"),
+    "q4_0": S.WORKLOADS["opt175b-q4_0"].scaled(d=1280, n=1111, r=64, act="sqrelu"),
+}
+
+
+@pytest.mark.parametrize("name,B", [("f16", 1), ("f16", 16), ("f32", 1), ("f32", 3), ("f32", 6),
+                                    ("q4_0", 1), ("q4_0", 8)])
+def test_squared_relu(name, B):
+    """Squared ReLU (h = max(0, a)^2) through the fused kernel (batch 1; f32 batch 3),
+    the gathered two-kernel path (f32 batch 6) and the matrix-core path (batch 8, 16)."""
+    wl = SQRELU_SMALL[name]
+    log(f"squared relu {name} B={B}")
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    if wl.hot_frac is not None:
+        Lh, n_hot = index_layer(L, dl, 256)
+    else:
+        Lh, n_hot = L, wl.n
+    buf = StepBuffers(dl, B, DEV)
+    for step in range(2):
+        x = S.make_x(wl, 0, step, B)
+        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step == 0)))
+        log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
+
+
 MFMA_SMALL = {
     "reglu-f16": S.WORKLOADS["llama70b-reglu-fp16"].scaled(d=768, n=1333, r=64),
     "relu-f16-split": S.WORKLOADS["opt30b-fp16"].scaled(d=512, n=1500, r=32),
