@@ -275,6 +275,20 @@ def test_split_points(small_f16, n_hot):
         check_step(L, n_hot, x, run_step(dl, buf, x, fused=(step == 0)))
 
 
+def test_two_mask_words_per_thread_ragged():
+    """32768 < n <= 65536 with n % 64 != 0: the fused kernel's prologue gives a
+    thread two mask words, and the last word has one valid bit."""
+    wl = S.WORKLOADS["opt30b-fp16"].scaled(d=256, n=40001, r=32)
+    L = S.make_layer(wl)
+    n_hot = 10000
+    dl = DeviceLayer.upload(L, DEV, n_hot=n_hot)
+    buf = StepBuffers(dl, 1, DEV)
+    for step in range(2):
+        x = S.make_x(wl, 0, step, 1)
+        e, namb, na = check_step(L, n_hot, x, run_step(dl, buf, x, fused=True))
+        log(f"  two words per thread, step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
+
+
 def test_wide_mask_compacted_before_fused_kernel():
     """n above the fused kernel's in-prologue mask bound (1024 words): the mask is
     compacted by its own kernel and the fused kernel reads the lists."""
