@@ -44,19 +44,22 @@ __global__ __launch_bounds__(THREADS) void k_pred_l1(const uint8_t* __restrict__
         for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
         constexpr int U = 4;                    // chunks in flight per thread
         for (int c0 = threadIdx.x; c0 < nch; c0 += THREADS * U) {
+            // branch-free: every weight and x load is issued (clamped addresses)
+            // before the first product waits, and a chunk or token past the end
+            // is dropped by a select after its product, keeping the summation
+            // order of the valid chunks
             u4 w[U];
 #pragma unroll
-            for (int q = 0; q < U; ++q)
-                if (c0 + THREADS * q < nch) w[q] = ld16_stream(row + 16 * (int64_t)(c0 + THREADS * q));
+            for (int q = 0; q < U; ++q) w[q] = ld16_stream(row + 16 * (int64_t)min(c0 + THREADS * q, nch - 1));
 #pragma unroll
             for (int q = 0; q < U; ++q) {
-                const int c = c0 + THREADS * q;
-                if (c < nch) {
+                const int c = min(c0 + THREADS * q, nch - 1);
+                const bool cv = c0 + THREADS * q < nch;
 #pragma unroll
-                    for (int b = 0; b < BT; ++b)
-                        if (b0 + b < B)
-                            acc[b] = Dot<WT, XT>::run(
-                                w[q], 0.0f, x + ((int64_t)(b0 + b) * d + c * EPC) * XB, acc[b]);
+                for (int b = 0; b < BT; ++b) {
+                    const float t = Dot<WT, XT>::run(
+                        w[q], 0.0f, x + ((int64_t)min(b0 + b, B - 1) * d + c * EPC) * XB, acc[b]);
+                    acc[b] = cv && b0 + b < B ? t : acc[b];
                 }
             }
         }
