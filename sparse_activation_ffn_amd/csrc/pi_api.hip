@@ -275,8 +275,9 @@ pi_status launch_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
 
 template <int WT, int XT, int BT>
 pi_status ffn_act(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
-    pi_status st = act != PI_REGLU ? launch_up<WT, XT, BT, RELU>(a, rows_cap, s)
-                                   : launch_up<WT, XT, BT, REGLU>(a, rows_cap, s);
+    pi_status st = act == PI_REGLU    ? launch_up<WT, XT, BT, REGLU>(a, rows_cap, s)
+                   : act == PI_SQRELU ? launch_up<WT, XT, BT, SQRELU>(a, rows_cap, s)
+                                      : launch_up<WT, XT, BT, RELU>(a, rows_cap, s);
     if (st != PI_OK) return st;
     return launch_down<WT, BT>(a, o, s);
 }
@@ -318,8 +319,9 @@ pi_status fused_nc_dispatch(const FfnArgs& a, const DownOut& o, hipStream_t s) {
 
 template <int WT, int XT, int BT>
 pi_status fused_act(const FfnArgs& a, const DownOut& o, int act, hipStream_t s) {
-    return act != PI_REGLU ? fused_nc_dispatch<WT, XT, BT, RELU>(a, o, s)
-                           : fused_nc_dispatch<WT, XT, BT, REGLU>(a, o, s);
+    return act == PI_REGLU    ? fused_nc_dispatch<WT, XT, BT, REGLU>(a, o, s)
+           : act == PI_SQRELU ? fused_nc_dispatch<WT, XT, BT, SQRELU>(a, o, s)
+                              : fused_nc_dispatch<WT, XT, BT, RELU>(a, o, s);
 }
 
 template <int WT, int XT>
@@ -373,8 +375,9 @@ pi_status mfma_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
 
 template <int WT>
 pi_status run_mfma_wt(const FfnArgs& a, const DownOut& o, int act, int rows_cap, hipStream_t s) {
-    if (act != PI_REGLU) TRY((mfma_up_mt<WT, RELU>(a, rows_cap, s)));
-    else TRY((mfma_up_mt<WT, REGLU>(a, rows_cap, s)));
+    if (act == PI_REGLU) TRY((mfma_up_mt<WT, REGLU>(a, rows_cap, s)));
+    else if (act == PI_SQRELU) TRY((mfma_up_mt<WT, SQRELU>(a, rows_cap, s)));
+    else TRY((mfma_up_mt<WT, RELU>(a, rows_cap, s)));
     const bool lists = a.idx[0] || a.idx[1];          // else dense rows
     switch (mfma_mt(a.B) * 2 + (lists ? 1 : 0)) {
     case 2: TRY((mfma_down<WT, false, 1>(a, o, s))); break;
@@ -445,7 +448,6 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.nparts = has_cold ? 2 : 1;
     a.rows[0] = hot->rows;
     a.rows[1] = has_cold ? cold->rows : 0;
-    a.square = hot->act == PI_SQRELU;              // squared ReLU: the ReLU kernels, h squared
     if (mask) {
         CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
         Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),

@@ -12,7 +12,7 @@ namespace pi {
 
 constexpr int WAVE = 64;
 enum { F32 = 0, F16 = 1, Q4 = 2 };
-enum { RELU = 0, REGLU = 1 };
+enum { RELU = 0, REGLU = 1, SQRELU = 2 };   // activations (SQRELU: max(0, a)^2)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));

@@ -136,6 +136,12 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
         mw[q] = 0;
         if (q < per) mw[q] = a.mask[min(w0 + q, words - 1)];
     }
+    // the weight and bias pointers and the output descriptor sit in
+    // kernel-argument cache lines that nothing above reads: fetch them now,
+    // while x and the mask are in flight, rather than as scalar-cache misses
+    // after the scan (it matters where a workgroup has few rows: OPT-style
+    // fp32 layer, 1.6 rows per workgroup)
+    asm volatile("" ::"s"(a.up[0]), "s"(a.bup[0]), "s"(o.partials), "s"(o.nch));
     store_x(xv0, 0);
     int H, C;
     int run = 0;                                       // rank of this thread's first set bit
@@ -343,7 +349,10 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         up += bu;
                         float hv;
                         if (ACT == RELU) {
-                            hv = up > 0.0f ? (a.square ? up * up : up) : 0.0f;
+                            hv = up > 0.0f ? up : 0.0f;
+                        } else if (ACT == SQRELU) {
+                            const float r = up > 0.0f ? up : 0.0f;
+                            hv = r * r;
                         } else {
                             gt += bg;
                             hv = (gt > 0.0f ? gt : 0.0f) * up;

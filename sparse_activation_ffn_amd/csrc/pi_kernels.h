@@ -255,7 +255,6 @@ struct FfnArgs {
     int n;
     int32_t* out_idx[2];
     int32_t* out_counts;
-    int square;              // squared ReLU (ACT == RELU kernels): h = max(0, up)^2
 };
 
 // Largest mask (in 64-bit words) whose compaction k_up does in LDS.
@@ -471,7 +470,10 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
                     up += a.bup[part] ? a.bup[part][row] : 0.0f;
                     float hv;
                     if (ACT == RELU) {
-                        hv = up > 0.0f ? (a.square ? up * up : up) : 0.0f;
+                        hv = up > 0.0f ? up : 0.0f;
+                    } else if (ACT == SQRELU) {
+                        const float r = up > 0.0f ? up : 0.0f;
+                        hv = r * r;
                     } else {
                         g += a.bgate[part] ? a.bgate[part][row] : 0.0f;
                         hv = (g > 0.0f ? g : 0.0f) * up;

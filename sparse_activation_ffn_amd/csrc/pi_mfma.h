@@ -277,7 +277,10 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const f4m (&acc)[N
                         const float up = acc[0][jn][mt][i] + bu;
                         float hv;
                         if (ACT == RELU) {
-                            hv = up > 0.0f ? (a.square ? up * up : up) : 0.0f;
+                            hv = up > 0.0f ? up : 0.0f;
+                        } else if (ACT == SQRELU) {
+                            const float r = up > 0.0f ? up : 0.0f;
+                            hv = r * r;
                         } else {
                             const float gt = acc[NM - 1][jn][mt][i] + bg;
                             hv = (gt > 0.0f ? gt : 0.0f) * up;
