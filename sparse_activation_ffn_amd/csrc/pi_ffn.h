@@ -139,8 +139,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     // the weight and bias pointers and the output descriptor sit in
     // kernel-argument cache lines that nothing above reads: fetch them now,
     // while x and the mask are in flight, rather than as scalar-cache misses
-    // after the scan (it matters where a workgroup has few rows: OPT-style
-    // fp32 layer, 1.6 rows per workgroup)
+    // after the scan
     asm volatile("" ::"s"(a.up[0]), "s"(a.bup[0]), "s"(o.partials), "s"(o.nch));
     store_x(xv0, 0);
     int H, C;
