@@ -3,9 +3,10 @@
 One step = one pass of the whole hot path over one token batch: predictor
 (both layers, threshold, union -> mask; `pi_predict`), then
 `pi_sparse_ffn_split` with the mask: compaction into hot/cold lists fused into
-the up/gate kernel, the sparse FFN over the hot and the cold partition, and
-the merge fused into the reduction of the down projection's partials.  Five
-kernels, no host synchronisation.
+the fused FFN kernel (up/gate, activation and down over the hot and the cold
+partition, one partial of y per workgroup), and the merge fused into the
+reduction of those partials.  Four kernels at batch 1 (five on the
+matrix-core path), no host synchronisation.
 
 Default workload: the OPT-30B-shaped ReLU layer (d_model 7168, d_ffn 28672,
 predictor rank 1024, fp16 weights, fp32 accumulation, batch 1), hot partition

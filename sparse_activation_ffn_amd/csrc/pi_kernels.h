@@ -1,7 +1,7 @@
 // pi_kernels.h -- HIP kernels of the predictor-gated sparse FFN (gfx950).
 //
-// One decode layer step runs six kernels on one stream, with the active
-// counts kept in device memory so the host never waits inside a step:
+// The kernels here, all on one stream with the active counts kept in device
+// memory so the host never waits inside a step:
 //   k_pred_l1   u = ReLU(P1t x)                       (dense rows of P1t)
 //   k_pred_l2   logit = P2t u + b2, > threshold, OR over tokens -> mask words
 //   k_compact   mask -> ascending hot / cold lists + device counts
@@ -10,6 +10,10 @@
 //               (column slice x neuron chunk) -> chunk partials
 //   k_reduce    chunk partials summed in a fixed order into y_hot, y_cold
 //               and y = y_hot + y_cold (the merge)
+// plus the offline index kernels.  A batch-1 step uses k_pred_l1, k_pred_l2,
+// then the fused FFN kernel of pi_ffn.h and its partial reduction; batches of
+// 2..64 use the matrix-core kernels of pi_mfma.h; k_up / k_down serve the
+// remaining shapes.
 // No kernel synchronises with another workgroup: kernel boundaries order the
 // steps, so no device-scope cache write-back is needed inside a kernel.
 // Method: PowerInfer pages -- CSDN article, sections on sparse activation
@@ -292,15 +296,10 @@ __device__ void scan_mask(const uint64_t* mask, int n, uint64_t* s_words, int* s
         s_words[w] = v;
         tot += __popcll(v);
     }
-    // inclusive scan of the per-thread totals: within each wave by shuffles, then
+    // inclusive scan of the per-thread totals: within each wave by DPP, then
     // across the NT / 64 wave totals
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
-    int inc = tot;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const int v = __shfl_up(inc, o, WAVE);
-        if (lane >= o) inc += v;
-    }
+    const int inc = wave_incl_scan(tot);
     if (lane == WAVE - 1) s_part[wv] = inc;
     __syncthreads();
     if (threadIdx.x == 0) {

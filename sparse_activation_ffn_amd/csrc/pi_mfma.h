@@ -181,12 +181,7 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
             tot += __popcll(v);
         }
         __shared__ int s_wtot[MFMA_WG / 64];
-        int inc = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += v;
-        }
+        const int inc = wave_incl_scan(tot);   // inclusive, DPP within the wave
         if (lane == 63) s_wtot[wv] = inc;
         __syncthreads();
         int before = 0, T = 0;
