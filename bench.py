@@ -15,16 +15,23 @@ indexed and permuted on the GPU before timing).  Steps rotate over INSTANCES
 device copies of the layer (same values, distinct addresses) with a fresh
 seeded x per step, so the 256 MB Infinity Cache cannot serve the weights.
 
-Reported: mean microseconds per layer step (`value`), achieved GB/s on the
-bytes the step must touch, per-kernel durations from HIP events recorded at
-each kernel's own dispatch, the dense FFN of the same layer, and the CPU
-oracle timed on a bounded sample on the host.
+Reported on one JSON line: mean microseconds per layer step (`value`, from a
+replay of the timed steps captured in one HIP graph) and its p10/p50/p90 over
+the steps (each step replayed from its own graph between HIP events), the
+achieved GB/s on the bytes the step must touch, per-kernel durations from HIP
+events recorded at each kernel's own dispatch, the roofline of the dominant
+kernel against the 8 TB/s HBM peak and against the attainable read rate of a
+plain read stream of the same size (`pi_stream_read`), the dense FFN of the
+same layer, the literal bias-free predictor as a secondary row, the
+Falcon-40B-shaped 60-layer stack (tokens/s of the FFN stack, default run
+only), and the CPU oracle timed on one host core and on all of them.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -36,8 +43,10 @@ if ROOT not in sys.path:
 
 METRIC = ("sparse-FFN µs/layer + achieved HBM GB/s on touched weights vs peak, batch 1")
 PEAK_HBM_GBPS = 8000.0
+TARGET_FRAC = 0.70                 # the sustained fraction of peak the step aims for
 INSTANCES = 8
-COPY_CAL_BYTES = 512 << 20     # reads 512 MiB, writes 512 MiB
+COPY_CAL_BYTES = 512 << 20         # reads 512 MiB, writes 512 MiB
+STREAM_BUF_BYTES = 1 << 30         # read-stream ceiling: offsets rotate through 1 GiB
 
 
 def log(*a):
@@ -97,42 +106,110 @@ def counter_traffic(wl_name, kernel):
     return k["read_bytes"] + k["write_bytes"]
 
 
-def cpu_baseline(wl, L, n_hot, B, budget_s=12.0):
-    """The oracle's layer step (predict, compact, sparse FFN per partition, merge) on the host."""
+def host_cpu():
+    """(model name, logical CPUs, threads the oracle may use on this host)."""
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    nproc = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = nproc
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(avail, int(env)) if env.isdigit() and int(env) > 0 else avail
+    return model, nproc, max(1, threads)
+
+
+def cpu_baseline(wl, L, n_hot, B, budget_s=8.0):
+    """The oracle's layer step (predict, compact, sparse FFN per partition, merge) on the
+    host: once single-threaded and once with its outer loops on all the cores this process
+    may use.  Each leg runs for about budget_s seconds."""
     from oracle import oracle as O
     from workload import synth as S
     hot = O.Part.from_layer(L, 0, n_hot)
     cold = O.Part.from_layer(L, n_hot, wl.n) if n_hot < wl.n else None
-    t0 = time.perf_counter()
-    steps = 0
-    while True:
-        x = S.make_x(wl, 0, 10_000 + steps, B)
-        O.layer_step(L.P1t, L.P2t, L.b2, L.threshold, hot, cold, x)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 200:
-            break
-    return {"value": round(el / steps * 1e6, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} layer steps of the same {wl.name} layer (batch {B}), "
-                      f"single-threaded C oracle, fp64 accumulation"}
+    model, nproc, threads = host_cpu()
+
+    def leg(k):
+        O.set_threads(k)
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            x = S.make_x(wl, 0, 10_000 + steps, B)
+            O.layer_step(L.P1t, L.P2t, L.b2, L.threshold, hot, cold, x)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or steps >= 400:
+                break
+        return el / steps * 1e6, steps
+
+    try:
+        one_us, one_n = leg(1)
+        all_us, all_n = leg(threads)
+    finally:
+        O.set_threads(1)
+    return {"value": round(all_us, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": f"{all_n} layer steps of the same {wl.name} layer (batch {B}), C oracle "
+                      f"(fp64 accumulation) with its outer loops on {threads} threads; "
+                      f"single-threaded: {one_n} steps",
+            "single_thread_us": round(one_us, 1), "nproc": nproc, "cpu_model": model}
 
 
-def stack_main(args, wl):
-    """The Falcon-40B-shaped FFN stack: 60 distinct layers, each with its own
-    predictor and a 20% hot partition indexed from 1024 profiling samples; a decode
-    step runs all 60 layer steps (fresh x per step and layer).  Layers are drawn on
-    the GPU (workload.synth.make_layer_device).  Reports µs per layer step and
-    tokens/s of the FFN stack."""
+def time_stream(pb, torch, nbytes, dev, launches=16):
+    """Attainable read rate of a plain stream of nbytes (per launch, HIP events at the
+    kernel's own dispatch), offsets rotating through a 1 GiB buffer so no launch reads
+    what the previous ones left in the caches."""
+    nbytes = max(16, nbytes // 16 * 16)
+    total = max(STREAM_BUF_BYTES, 8 * nbytes)
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    sink = torch.empty(pb.PI_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    slots = max(1, total // nbytes)
+    for i in range(2):
+        pb.pi_stream_read(buf[(i % slots) * nbytes:], nbytes, sink)
+    torch.cuda.synchronize()
+    pb.pi_kernel_timer_start(pb.PI_K_STREAM, launches)
+    for i in range(launches):
+        pb.pi_stream_read(buf[(i % slots) * nbytes:], nbytes, sink)
+    ms, k = pb.pi_kernel_timer_stop(pb.PI_K_STREAM)
+    del buf
+    return nbytes / (ms / k * 1e-3) / 1e9
+
+
+def replay_per_step(torch, step, idxs):
+    """Device time of each step replayed from its own graph between HIP events."""
+    graphs = []
+    for i in idxs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for g in graphs[:2]:
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+    ev[0].record()
+    for g, e in zip(graphs, ev[1:]):
+        g.replay()
+        e.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev[:-1], ev[1:])])
+
+
+def draw_stack(wl, dev):
+    """The Falcon-40B-shaped stack: 60 distinct layers drawn on the GPU
+    (workload.synth.make_layer_device), each profiled on 1024 samples, indexed under its
+    20% budget and permuted, all on the GPU."""
     import torch
-    from sparse_activation_ffn_amd import binding as pb
-    from sparse_activation_ffn_amd.layer import DeviceLayer, StepBuffers
+    from sparse_activation_ffn_amd.layer import DeviceLayer
     from workload import synth as S
-    dev = "cuda:0"
-    B, K, W = args.batch, args.steps, args.warmup
-    NL = wl.layers
     layers = []
-    log(f"[bench] drawing, profiling and indexing {NL} layers on the GPU ...")
-    for li in range(NL):
+    for li in range(wl.layers):
         ly = DeviceLayer.from_tensors(wl, S.make_layer_device(wl, li, dev))
         g = torch.Generator(device=dev)
         g.manual_seed(S.SEED + 7 * li + 1)
@@ -143,10 +220,24 @@ def stack_main(args, wl):
         layers.append(ly)
         del X
     torch.cuda.synchronize()
+    return layers
+
+
+def run_stack(wl, B, K, W, dev):
+    """Decode steps over the whole stack (fresh x per step and layer).  Returns the
+    summary dict: µs per layer step, tokens/s of the FFN stack, touched-byte rate, and
+    per-kernel durations over the first timed step."""
+    import torch
+    from sparse_activation_ffn_amd import binding as pb
+    from sparse_activation_ffn_amd.layer import StepBuffers
+    NL = wl.layers
+    t0 = time.perf_counter()
+    layers = draw_stack(wl, dev)
+    setup_s = time.perf_counter() - t0
     descs = [(ly.predictor(), ly.parts()) for ly in layers]
     buf = StepBuffers(layers[0], B, dev)
     gx = torch.Generator(device=dev)
-    gx.manual_seed(S.SEED + 99)
+    gx.manual_seed(20231216 + 99)
     xs = torch.randn(W + K, NL, B, wl.d, generator=gx, device=dev).to(torch.float16)
 
     def layer_step(s, li):
@@ -155,7 +246,6 @@ def stack_main(args, wl):
         pb.pi_predict(pred, x, buf.mask, None, None, buf.ws)
         pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, None, None, buf.y, buf.ws, mask=buf.mask)
 
-    log(f"[bench] warmup {W} + timed {K} decode steps x {NL} layers ...")
     for s in range(W):
         for li in range(NL):
             layer_step(s, li)
@@ -173,7 +263,6 @@ def stack_main(args, wl):
     e1.record()
     torch.cuda.synchronize()
     us_layer = e0.elapsed_time(e1) * 1e3 / (K * NL)
-    # per-kernel durations and active counts over the first timed step
     kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2, "k_ffn": pb.PI_K_FFN,
             "k_reduce": pb.PI_K_REDUCE}
     for kid in kids.values():
@@ -184,39 +273,37 @@ def stack_main(args, wl):
         active.append(int(buf.counts.sum().item()))
     kern = {name: pb.pi_kernel_timer_stop(kid) for name, kid in kids.items()}
     kern_us = {k: ms * 1e3 / max(n, 1) for k, (ms, n) in kern.items() if n}
-    kb = [kernel_bytes(wl, B, a) for a in active]
-    kb_mean = {k: float(np.mean([b[k] for b in kb])) for k in kern_us}
-    dom = max(kern_us, key=kern_us.get)
-    dom_gbps = kb_mean[dom] / (kern_us[dom] * 1e-6) / 1e9
     touched = float(np.mean([step_bytes(wl, B, a) for a in active]))
     gbps = touched / (us_layer * 1e-6) / 1e9
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] CPU oracle baseline (host-drawn layer 59) ...")
-        L = S.make_layer(wl, layer=NL - 1)
-        cpu = cpu_baseline(wl, L, int(wl.hot_frac * wl.n), B)
-        cpu["sample"] += " (layer 59 unpermuted, first 20% of rows as the hot partition)"
+    del layers, descs, xs
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "layers": NL, "batch": B, "steps": K, "warmup": W,
+            "us_per_layer": round(us_layer, 3), "ms_per_token": round(us_layer * NL / 1e3, 4),
+            "tokens_per_s_ffn_stack": round(1e6 / (us_layer * NL), 1),
+            "mean_active": round(float(np.mean(active)), 1),
+            "touched_bytes_per_layer_step": round(touched),
+            "achieved_gbps_touched": round(gbps, 1),
+            "frac_of_peak_touched": round(gbps / PEAK_HBM_GBPS, 4),
+            "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+            "dense_gemv_tokens_per_s_at_peak": round(
+                PEAK_HBM_GBPS * 1e9 / (NL * (2 * wl.n * wrow_bytes(wl) + 4 * wl.n)), 1),
+            "setup_s": round(setup_s, 1), "timing": "hip_graph",
+            "data": "synthetic, layers drawn on the GPU"}
+
+
+def stack_main(args, wl):
+    """`--workload falcon40b-stack-fp16`: the stack on its own JSON line (µs per layer
+    step as `value`)."""
+    s = run_stack(wl, args.batch, args.steps, args.warmup, "cuda:0")
     out = {
-        "metric": METRIC, "value": round(us_layer, 3), "unit": "us/layer", "n_gpus": 1,
-        "steps": K, "warmup": W, "ms_per_step": round(us_layer * NL / 1e3, 6),
+        "metric": METRIC, "value": s["us_per_layer"], "unit": "us/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": s["ms_per_token"],
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": NL, "d_model": wl.d, "d_ffn": wl.n,
-                   "predictor_rank": wl.r, "batch": B, "weights": wl.wdtype,
-                   "accumulate": "f32", "hot_fraction": wl.hot_frac,
-                   "mean_active": round(float(np.mean(active)), 1)},
-        "timing": "hip_graph",
-        "tokens_per_s_ffn_stack": round(1e6 / (us_layer * NL), 1),
-        "touched_bytes_per_layer_step": round(touched),
-        "achieved_gbps_touched": round(gbps, 1),
-        "frac_of_peak_touched": round(gbps / PEAK_HBM_GBPS, 4),
-        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1),
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
-                     "algorithmic_bytes": round(kb_mean[dom]),
-                     "traffic": counter_traffic(wl.name, dom)},
-        "cpu_baseline": cpu,
+        "config": {"workload": wl.name, "layers": wl.layers, "d_model": wl.d, "d_ffn": wl.n,
+                   "predictor_rank": wl.r, "batch": args.batch, "weights": wl.wdtype,
+                   "accumulate": "f32", "hot_fraction": wl.hot_frac},
+        "stack": s,
     }
     print(json.dumps(out), flush=True)
 
@@ -229,8 +316,14 @@ def main():
     ap.add_argument("--workload", default="opt30b-fp16")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--instances", type=int, default=INSTANCES)
+    ap.add_argument("--stack-steps", type=int, default=16,
+                    help="decode steps of the Falcon-40B-shaped stack in the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only (no per-step graphs, literal predictor, stream "
+                         "ceiling): for profiler runs")
     ap.add_argument("--cold-host", action="store_true",
                     help="place the cold partition's weight rows in pinned host memory "
                          "(capacity tier), read by the kernels over the host link")
@@ -277,8 +370,10 @@ def main():
     xs = [torch.from_numpy(S.make_x(wl, 0, s, B)).to(dev) for s in range(W + K)]
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, literal=False):
         pred, (hot, cold) = descs[i % len(layers)]
+        if literal:
+            pred = lit_preds[i % len(layers)]
         x = xs[i]
         pb.pi_predict(pred, x, buf.mask, None, None, buf.ws)
         pb.pi_sparse_ffn_split(hot, cold, x, buf.lists, None, None, buf.y, buf.ws, mask=buf.mask)
@@ -296,7 +391,6 @@ def main():
     torch.cuda.synchronize()
     us_step_eager = e0.elapsed_time(e1) * 1e3 / K
     # the timed steps captured once into a HIP graph and replayed: device time only
-    graph = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -309,6 +403,7 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         us_step = e0.elapsed_time(e1) * 1e3 / K
+        del graph
     else:
         us_step = us_step_eager
 
@@ -318,7 +413,7 @@ def main():
             "k_compact": pb.PI_K_COMPACT, "k_up": pb.PI_K_UP, "k_down": pb.PI_K_DOWN,
             "k_ffn": pb.PI_K_FFN, "k_reduce": pb.PI_K_REDUCE}
     for kid in kids.values():
-        pb.pi_kernel_timer_start(kid, K)
+        pb.pi_kernel_timer_start(kid, 2 * K)
     active = []
     hot_active = []
     for i in range(W, W + K):
@@ -333,12 +428,56 @@ def main():
     kb_mean = {k: float(np.mean([b[k] for b in kb])) for k in kb[0]}
     touched = float(np.mean([step_bytes(wl, B, a) for a in active]))
     gbps_touched = touched / (us_step * 1e-6) / 1e9
-    dom = max(kern_us, key=kern_us.get)
+    ran = {k for k in kern_us if kern_ms[k][1] > 0}
+    dom = max(ran, key=lambda k: kern_us[k])
     dom_gbps = kb_mean[dom] / (kern_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
                 "algorithmic_bytes": round(kb_mean[dom]),
-                "traffic": counter_traffic(wl.name, dom)}
+                "traffic": counter_traffic(wl.name, dom), "target_frac": TARGET_FRAC}
+
+    extras = {}
+    if not args.no_extras:
+        log("[bench] per-step graphs, stream ceiling, literal predictor ...")
+        per = replay_per_step(torch, step, list(range(W, W + K)))
+        extras["step_us_percentiles"] = {
+            "p10": round(float(np.percentile(per, 10)), 3),
+            "p50": round(float(np.percentile(per, 50)), 3),
+            "p90": round(float(np.percentile(per, 90)), 3),
+            "how": "each timed step replayed from its own HIP graph between HIP events"}
+        att = time_stream(pb, torch, int(kb_mean[dom]), dev)
+        att_long = time_stream(pb, torch, STREAM_BUF_BYTES // 2, dev, launches=8)
+        roofline["attainable"] = round(att, 1)
+        roofline["frac_of_attainable"] = round(dom_gbps / att, 4)
+        roofline["attainable_long_stream"] = round(att_long, 1)
+        roofline["attainable_note"] = ("plain read stream (pi_stream_read) of the dominant "
+                                       "kernel's algorithmic bytes per launch; the long stream "
+                                       "reads 512 MiB per launch")
+        extras["step_frac_of_attainable_long_stream"] = round(gbps_touched / att_long, 4)
+        # the literal predictor: the configs' random predictor with no output bias and
+        # threshold 0 fires for about half of the neurons
+        lit_preds = [pb.make_predictor(ly.P1t, ly.P2t, None, ly.threshold) for ly in layers]
+        for i in range(W, W + 3):
+            step(i, literal=True)
+        torch.cuda.synchronize()
+        KL = max(10, K // 4)
+        lit_active = []
+        e0.record()
+        for i in range(W, W + KL):
+            step(i, literal=True)
+        e1.record()
+        torch.cuda.synchronize()
+        lit_us = e0.elapsed_time(e1) * 1e3 / KL
+        for i in range(W, W + 4):
+            step(i, literal=True)
+            lit_active.append(int(buf.counts.sum().item()))
+        la = float(np.mean(lit_active))
+        extras["literal_predictor"] = {
+            "us_per_step_eager": round(lit_us, 3), "mean_active": round(la, 1),
+            "density": round(la / wl.n, 4),
+            "touched_bytes_per_step": round(step_bytes(wl, B, la)),
+            "achieved_gbps_touched": round(step_bytes(wl, B, la) / (lit_us * 1e-6) / 1e9, 1),
+            "note": "predictor without its output bias (b2 = 0, threshold 0), eager launches"}
 
     dense = None
     if not args.no_dense:
@@ -354,9 +493,19 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         dense_us = e0.elapsed_time(e1) * 1e3 / KD
-        dense_bytes = 2 * wl.n * wrow_bytes(wl) + 4 * wl.n
+        dense_bytes = (3 if wl.act == "reglu" else 2) * wl.n * wrow_bytes(wl) + 4 * wl.n
         dense = {"us": round(dense_us, 2), "gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
-                 "speedup_sparse_step_vs_dense_ffn": round(dense_us / us_step, 2)}
+                 "speedup_sparse_step_vs_dense_ffn": round(dense_us / us_step, 2),
+                 "speedup_vs_dense_gemv_at_peak": round(
+                     dense_bytes / (PEAK_HBM_GBPS * 1e3) / us_step, 2)}
+
+    stack = None
+    if (not args.no_stack and args.workload == "opt30b-fp16" and B == 1 and not args.cold_host
+            and not args.eager):
+        del layers, descs
+        torch.cuda.empty_cache()
+        log("[bench] Falcon-40B-shaped 60-layer stack ...")
+        stack = run_stack(S.WORKLOADS["falcon40b-stack-fp16"], 1, args.stack_steps, 2, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,7 +526,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "d_model": wl.d, "d_ffn": wl.n, "predictor_rank": wl.r,
                    "batch": B, "weights": wl.wdtype, "accumulate": "f32",
-                   "hot_fraction": wl.hot_frac, "n_hot": n_hot, "instances": len(layers),
+                   "hot_fraction": wl.hot_frac, "n_hot": n_hot, "instances": args.instances,
                    "mean_active": round(mean_active, 1),
                    "mean_hot_active": round(float(np.mean(hot_active)), 1)},
         "timing": "eager" if args.eager else "hip_graph",
@@ -385,12 +534,13 @@ def main():
         "touched_bytes_per_step": round(touched),
         "achieved_gbps_touched": round(gbps_touched, 1),
         "frac_of_peak_touched": round(gbps_touched / PEAK_HBM_GBPS, 4),
-        "kernels_us": {k: round(v, 3) for k, v in kern_us.items() if kern_ms[k][1] > 0},
+        "kernels_us": {k: round(kern_us[k], 3) for k in sorted(ran)},
         "cold_tier": "host" if args.cold_host and n_hot < wl.n else "hbm",
         "cold_bytes_per_step": round(float(np.mean([a - h for a, h in zip(active, hot_active)]))
                                      * ((3 if wl.act == "reglu" else 2) * wrow_bytes(wl) + 4)),
-        "kernel_bytes": {k: round(kb_mean[k]) for k in kern_us if kern_ms[k][1] > 0},
-        "roofline": roofline, "dense_ffn": dense, "cpu_baseline": cpu,
+        "kernel_bytes": {k: round(kb_mean[k]) for k in sorted(ran)},
+        "roofline": roofline, **extras, "dense_ffn": dense, "falcon40b_stack": stack,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

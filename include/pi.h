@@ -148,16 +148,31 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Compacts mask [ceil(n/64)] into the ascending active lists of `lists`
- * (one workgroup; no workspace).
+ * Compaction of the predicted set into the lists the partitions compute (CSDN
+ * article, section on sparse activation: only the predicted neurons are
+ * computed; hybrid-design figure: the predicted ids, e.g. 3, 4, 5, go to the
+ * partition that holds each one).  mask [ceil(n/64)] uint64 device, 8-byte
+ * aligned, as written by pi_predict; bits >= n are ignored.  lists (see
+ * pi_active_lists) receives hot ids < n_hot and cold ids - n_hot, both
+ * ascending, and the device counts; the lists must hold n_hot and n - n_hot
+ * entries.  One workgroup; no workspace.  Errors (NULL mask or lists, n out
+ * of 1..2^24, n_hot outside 0..n, a list missing for a non-empty partition,
+ * misalignment) enqueue nothing.
  */
 pi_status pi_compact_active(const uint64_t* mask, int32_t n, const pi_active_lists* lists,
                             void* stream);
 
 /*
- * Sparse FFN over one partition: y [B][d] float32 (overwritten) =
- * sum over the first *count entries of idx (ascending ids < part->rows) of
- * h_i * W_downT[i][:].  `count` is a device int32 scalar.
+ * Sparse FFN over one partition (CSDN article, section on sparse activation:
+ * neuron-aware operators read and compute only the rows of the predicted
+ * neurons; neurons that do not fire contribute nothing):
+ *   y[b][:] = sum over the first *count entries i of idx of h_bi * W_downT[i][:]
+ * with h as in pi_ffn_part, every token over the same list.  x [B][d]
+ * (xdtype PI_F32 or PI_F16, 16-byte aligned); idx int32 device, ascending ids
+ * < part->rows (an id outside the partition contributes nothing); count a
+ * device int32 scalar (clamped to 0..part->rows); y [B][d] float32,
+ * overwritten.  Rows not listed are never read.  Needs a workspace
+ * (pi_workspace_bytes); errors enqueue nothing.
  */
 pi_status pi_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
                         const int32_t* idx, const int32_t* count, float* y,
@@ -246,6 +261,17 @@ pi_status pi_permute_rows(const void* src, void* dst, const int32_t* perm, int32
  */
 pi_status pi_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/*
+ * Plain read stream of `bytes` bytes of src (bytes % 16 == 0, src 16-byte
+ * aligned; device or pinned host memory): the attainable read bandwidth of
+ * the memory src lives in, the ceiling the weight-streaming kernels are
+ * measured against beside the 8 TB/s HBM peak.  sink [PI_STREAM_SINK_WORDS]
+ * uint32 device, out: one xor of the words read per workgroup (their value
+ * means nothing; they keep the reads from being optimised away).
+ */
+#define PI_STREAM_SINK_WORDS 2048
+pi_status pi_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Kernel ids for the timing hooks below. */
 enum {
     PI_K_PRED_L1 = 0,     /* predictor first layer */
@@ -260,7 +286,8 @@ enum {
     PI_K_REDUCE = 9,      /* partials of y -> y_hot, y_cold, y (fused merge) */
     PI_K_FFN = 10,        /* fused compaction + up/gate + activation + down (batch <= 4) */
     PI_K_ACCUMULATE = 11, /* online activation counts from a mask */
-    PI_K_COUNT = 12
+    PI_K_STREAM = 12,     /* plain read stream (attainable bandwidth) */
+    PI_K_COUNT = 13
 };
 
 /*

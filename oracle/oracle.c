@@ -53,6 +53,19 @@
 #include <stdlib.h>
 #include <string.h>
 
+/*
+ * Threads: every routine runs single-threaded unless or_set_threads(k > 1) is
+ * called; then the independent outer loops (predictor rows, neurons of a
+ * list, output columns, profiled rows) are shared among k OpenMP threads.
+ * Each output value is still computed by one thread with the same operations
+ * in the same order, so the results are bit-identical for any thread count.
+ * (Used to time the oracle on all of a host's cores.)
+ */
+static int or_nthreads = 1;
+
+void or_set_threads(int k) { or_nthreads = k < 1 ? 1 : k; }
+int or_get_threads(void) { return or_nthreads; }
+
 enum { OR_F32 = 0, OR_F16 = 1, OR_Q4_0 = 2 };
 enum { OR_RELU = 0, OR_REGLU = 1, OR_SQRELU = 2 };
 enum { OR_OK = 0, OR_BAD = 1 };
@@ -97,11 +110,13 @@ double or_q4_0_element(const uint8_t* row, int64_t d, int64_t k)
     return (double)(q - 8) * or_half_to_double(sbits);
 }
 
-/* Row `row` of a [rows][d] matrix, decoded to double. */
-void or_load_row(const void* W, int wdtype, int64_t d, int64_t row, double* out)
+/* Elements [k0, k1) of row `row` of a [rows][d] matrix, decoded to double
+ * into out[k0 .. k1). */
+static void or_load_row_range(const void* W, int wdtype, int64_t d, int64_t row, int64_t k0,
+                              int64_t k1, double* out)
 {
     const uint8_t* base = (const uint8_t*)W + row * or_row_bytes(wdtype, d);
-    for (int64_t k = 0; k < d; ++k) {
+    for (int64_t k = k0; k < k1; ++k) {
         if (wdtype == OR_F32) {
             float v;
             memcpy(&v, base + 4 * k, 4);
@@ -114,6 +129,12 @@ void or_load_row(const void* W, int wdtype, int64_t d, int64_t row, double* out)
             out[k] = or_q4_0_element(base, d, k);
         }
     }
+}
+
+/* Row `row` of a [rows][d] matrix, decoded to double. */
+void or_load_row(const void* W, int wdtype, int64_t d, int64_t row, double* out)
+{
+    or_load_row_range(W, wdtype, d, row, 0, d, out);
 }
 
 /* Token b of an input matrix x[B][d] stored as f32 or f16. */
@@ -149,30 +170,48 @@ int or_predict(int64_t d, int64_t n, int64_t r, int pdtype, const void* P1t, con
         return OR_BAD;
     int64_t words = (n + 63) / 64;
     double* xb = malloc(sizeof(double) * d);
-    double* row = malloc(sizeof(double) * (d > r ? d : r));
     double* u = malloc(sizeof(double) * r);
-    if (!xb || !row || !u) { free(xb); free(row); free(u); return OR_BAD; }
+    unsigned char* fire = calloc((size_t)n, 1);     /* bit 0: > threshold, bit 1: in float32 */
+    if (!xb || !u || !fire) { free(xb); free(u); free(fire); return OR_BAD; }
+    int bad = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        or_load_x(x, xdtype, d, b, xb);
+#pragma omp parallel num_threads(or_nthreads) if (or_nthreads > 1)
+        {
+            double* row = malloc(sizeof(double) * (d > r ? d : r));
+            if (!row) {
+#pragma omp atomic write
+                bad = 1;
+            }
+#pragma omp for schedule(static)
+            for (int64_t j = 0; j < r; ++j) {
+                if (!row) continue;
+                or_load_row(P1t, pdtype, d, j, row);
+                double a = or_dot(row, xb, d);
+                u[j] = a > 0.0 ? a : 0.0;
+            }
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < n; ++i) {
+                if (!row) continue;
+                or_load_row(P2t, pdtype, r, i, row);
+                double lg = or_dot(row, u, r) + (b2 ? (double)b2[i] : 0.0);
+                if (logits) logits[b * n + i] = lg;
+                if (lg > threshold) fire[i] |= 1;
+                if ((float)lg > (float)threshold) fire[i] |= 2;
+            }
+            free(row);
+        }
+    }
     for (int64_t w = 0; w < words; ++w) {
         mask[w] = 0;
         if (mask32) mask32[w] = 0;
     }
-    for (int64_t b = 0; b < B; ++b) {
-        or_load_x(x, xdtype, d, b, xb);
-        for (int64_t j = 0; j < r; ++j) {
-            or_load_row(P1t, pdtype, d, j, row);
-            double a = or_dot(row, xb, d);
-            u[j] = a > 0.0 ? a : 0.0;
-        }
-        for (int64_t i = 0; i < n; ++i) {
-            or_load_row(P2t, pdtype, r, i, row);
-            double lg = or_dot(row, u, r) + (b2 ? (double)b2[i] : 0.0);
-            if (logits) logits[b * n + i] = lg;
-            if (lg > threshold) mask[i / 64] |= (uint64_t)1 << (i % 64);
-            if (mask32 && (float)lg > (float)threshold) mask32[i / 64] |= (uint64_t)1 << (i % 64);
-        }
+    for (int64_t i = 0; i < n; ++i) {
+        if (fire[i] & 1) mask[i / 64] |= (uint64_t)1 << (i % 64);
+        if (mask32 && (fire[i] & 2)) mask32[i / 64] |= (uint64_t)1 << (i % 64);
     }
-    free(xb); free(row); free(u);
-    return OR_OK;
+    free(xb); free(u); free(fire);
+    return bad ? OR_BAD : OR_OK;
 }
 
 /* ---- compaction ------------------------------------------------------- */
@@ -224,37 +263,62 @@ int or_sparse_ffn(const or_part* p, const void* x, int xdtype, int64_t B, const 
     int64_t d = p->d;
     if (d <= 0 || B < 0 || count < 0 || (p->act == OR_REGLU && !p->W_gate))
         return OR_BAD;
+    for (int64_t t = 0; t < count; ++t)
+        if (idx[t] < 0 || idx[t] >= p->rows) return OR_BAD;
+    enum { COLS = 256 };                           /* output columns per work item */
+    const int64_t nblk = (d + COLS - 1) / COLS;
     double* xb = malloc(sizeof(double) * d);
-    double* row = malloc(sizeof(double) * d);
-    if (!xb || !row) { free(xb); free(row); return OR_BAD; }
+    double* h = malloc(sizeof(double) * (count > 0 ? count : 1));
+    if (!xb || !h) { free(xb); free(h); return OR_BAD; }
+    int bad = 0;
     for (int64_t b = 0; b < B; ++b) {
         double* yb = y + b * d;
-        for (int64_t k = 0; k < d; ++k)
-            yb[k] = 0.0;
         or_load_x(x, xdtype, d, b, xb);
-        for (int64_t t = 0; t < count; ++t) {
-            int64_t i = idx[t];
-            if (i < 0 || i >= p->rows) { free(xb); free(row); return OR_BAD; }
-            or_load_row(p->W_up, p->wdtype, d, i, row);
-            double up = or_dot(row, xb, d) + (p->b_up ? (double)p->b_up[i] : 0.0);
-            double h;
-            if (p->act == OR_RELU) {
-                h = up > 0.0 ? up : 0.0;
-            } else if (p->act == OR_SQRELU) {
-                const double r = up > 0.0 ? up : 0.0;
-                h = r * r;
-            } else {
-                or_load_row(p->W_gate, p->wdtype, d, i, row);
-                double g = or_dot(row, xb, d) + (p->b_gate ? (double)p->b_gate[i] : 0.0);
-                h = (g > 0.0 ? g : 0.0) * up;
+#pragma omp parallel num_threads(or_nthreads) if (or_nthreads > 1)
+        {
+            double* row = malloc(sizeof(double) * d);
+            if (!row) {
+#pragma omp atomic write
+                bad = 1;
             }
-            or_load_row(p->W_downT, p->wdtype, d, i, row);
-            for (int64_t k = 0; k < d; ++k)
-                yb[k] += h * row[k];
+            /* h of every listed neuron */
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < count; ++t) {
+                if (!row) continue;
+                int64_t i = idx[t];
+                or_load_row(p->W_up, p->wdtype, d, i, row);
+                double up = or_dot(row, xb, d) + (p->b_up ? (double)p->b_up[i] : 0.0);
+                double hv;
+                if (p->act == OR_RELU) {
+                    hv = up > 0.0 ? up : 0.0;
+                } else if (p->act == OR_SQRELU) {
+                    const double r = up > 0.0 ? up : 0.0;
+                    hv = r * r;
+                } else {
+                    or_load_row(p->W_gate, p->wdtype, d, i, row);
+                    double g = or_dot(row, xb, d) + (p->b_gate ? (double)p->b_gate[i] : 0.0);
+                    hv = (g > 0.0 ? g : 0.0) * up;
+                }
+                h[t] = hv;
+            }
+            /* y_b[k] = sum over the list, in its order, of h_i * W_downT[i][k] */
+#pragma omp for schedule(static)
+            for (int64_t cb = 0; cb < nblk; ++cb) {
+                if (!row) continue;
+                const int64_t k0 = cb * COLS, k1 = k0 + COLS < d ? k0 + COLS : d;
+                for (int64_t k = k0; k < k1; ++k)
+                    yb[k] = 0.0;
+                for (int64_t t = 0; t < count; ++t) {
+                    or_load_row_range(p->W_downT, p->wdtype, d, idx[t], k0, k1, row);
+                    for (int64_t k = k0; k < k1; ++k)
+                        yb[k] += h[t] * row[k];
+                }
+            }
+            free(row);
         }
     }
-    free(xb); free(row);
-    return OR_OK;
+    free(xb); free(h);
+    return bad ? OR_BAD : OR_OK;
 }
 
 /* The dense FFN: the sparse FFN with the list [0, rows). */
@@ -294,26 +358,37 @@ int or_profile_counts(const or_part* p, const void* X, int xdtype, int64_t S, ui
     const float* bias = p->act == OR_REGLU ? p->b_gate : p->b_up;
     if (d <= 0 || S < 0 || !W) return OR_BAD;
     double* xs = malloc(sizeof(double) * d * (S > 0 ? S : 1));
-    double* row = malloc(sizeof(double) * d);
-    if (!xs || !row) { free(xs); free(row); return OR_BAD; }
+    if (!xs) return OR_BAD;
     for (int64_t s = 0; s < S; ++s)
         or_load_x(X, xdtype, d, s, xs + s * d);
-    for (int64_t i = 0; i < p->rows; ++i) {
-        or_load_row(W, p->wdtype, d, i, row);
-        double bi = bias ? (double)bias[i] : 0.0;
-        uint32_t c = 0, c32 = 0, a = 0;
-        for (int64_t s = 0; s < S; ++s) {
-            double pre = or_dot(row, xs + s * d, d) + bi;
-            c += pre > 0.0;
-            c32 += (float)pre > 0.0f;
-            a += fabs(pre) <= band;
+    int bad = 0;
+#pragma omp parallel num_threads(or_nthreads) if (or_nthreads > 1)
+    {
+        double* row = malloc(sizeof(double) * d);
+        if (!row) {
+#pragma omp atomic write
+            bad = 1;
         }
-        counts[i] = c;
-        if (counts32) counts32[i] = c32;
-        if (amb) amb[i] = a;
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < p->rows; ++i) {
+            if (!row) continue;
+            or_load_row(W, p->wdtype, d, i, row);
+            double bi = bias ? (double)bias[i] : 0.0;
+            uint32_t c = 0, c32 = 0, a = 0;
+            for (int64_t s = 0; s < S; ++s) {
+                double pre = or_dot(row, xs + s * d, d) + bi;
+                c += pre > 0.0;
+                c32 += (float)pre > 0.0f;
+                a += fabs(pre) <= band;
+            }
+            counts[i] = c;
+            if (counts32) counts32[i] = c32;
+            if (amb) amb[i] = a;
+        }
+        free(row);
     }
-    free(xs); free(row);
-    return OR_OK;
+    free(xs);
+    return bad ? OR_BAD : OR_OK;
 }
 
 static const uint32_t* or_sort_counts;

@@ -31,8 +31,8 @@ def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (IEEE semantics: no fast-math, no contraction)."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
-                               "-Wall", "-Wextra", SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                               "-shared", "-Wall", "-Wextra", SRC, "-o", tmp, "-lm"])
         os.replace(tmp, LIB)
     return LIB
 
@@ -45,6 +45,10 @@ def lib():
     if _lib is None:
         _lib = C.CDLL(build())
         P, I64, I, D = C.c_void_p, C.c_int64, C.c_int, C.c_double
+        _lib.or_set_threads.argtypes = [I]
+        _lib.or_set_threads.restype = None
+        _lib.or_get_threads.argtypes = []
+        _lib.or_get_threads.restype = I
         _lib.or_half_to_double.argtypes = [C.c_uint16]
         _lib.or_half_to_double.restype = D
         _lib.or_q4_0_element.argtypes = [P, I64, I64]
@@ -108,6 +112,16 @@ class Part:
         sl = lambda a: None if a is None else a[lo:hi]  # noqa: E731
         return cls(L.d, sl(L.W_up), sl(L.W_downT), act=L.wl.act, W_gate=sl(L.W_gate),
                    b_up=sl(L.b_up), b_gate=sl(L.b_gate), q4=(L.wl.wdtype == "q4_0"))
+
+
+def set_threads(k: int) -> None:
+    """Share the oracle's independent outer loops among k threads (1 = serial).
+    Results are bit-identical for every k."""
+    lib().or_set_threads(int(k))
+
+
+def get_threads() -> int:
+    return int(lib().or_get_threads())
 
 
 def half_to_double(bits: int) -> float:

@@ -21,13 +21,14 @@ PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
 PI_RELU, PI_REGLU, PI_SQRELU = 0, 1, 2
 PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
- PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_COUNT) = range(13)
+ PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_STREAM, PI_K_COUNT) = range(14)
+PI_STREAM_SINK_WORDS = 2048
 
 # every symbol include/pi.h declares
 EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_active",
            "pi_sparse_ffn", "pi_sparse_ffn_split", "pi_merge", "pi_dense_ffn",
            "pi_profile_counts", "pi_build_neuron_index", "pi_accumulate_mask", "pi_permute_rows",
-           "pi_copy",
+           "pi_copy", "pi_stream_read",
            "pi_kernel_timer_start", "pi_kernel_timer_stop", "pi_kernel_name", "pi_status_string",
            "pi_last_error")
 
@@ -82,6 +83,7 @@ def lib() -> C.CDLL:
         "pi_accumulate_mask": ([P, I32, P, P], I32),
         "pi_permute_rows": ([P, P, P, I32, I64, P], I32),
         "pi_copy": ([P, P, I64, P], I32),
+        "pi_stream_read": ([P, I64, P, P], I32),
         "pi_kernel_timer_start": ([I32, I32], I32),
         "pi_kernel_timer_stop": ([I32, P, P], I32),
         "pi_kernel_name": ([I32], C.c_char_p),
@@ -203,6 +205,10 @@ def pi_permute_rows(src, dst, perm, rows: int, row_bytes: int, stream=None):
 
 def pi_copy(src, dst, nbytes: int, stream=None):
     _check(lib().pi_copy(ptr(src), ptr(dst), nbytes, stream_handle(stream)))
+
+
+def pi_stream_read(src, nbytes: int, sink, stream=None):
+    _check(lib().pi_stream_read(ptr(src), nbytes, ptr(sink), stream_handle(stream)))
 
 
 def pi_kernel_timer_start(kid: int, max_launches: int):

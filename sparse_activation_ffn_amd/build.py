@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpi.so")
 SOURCES = [os.path.join(CSRC, "pi_api.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("pi_device.h", "pi_kernels.h")] + \
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")] + \
     [os.path.join(INCLUDE, "pi.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

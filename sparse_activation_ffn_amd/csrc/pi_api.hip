@@ -108,10 +108,11 @@ int mfma_chunks(int d) {
     return k < 2 ? 2 : k > NCH_MAX ? NCH_MAX : k;
 }
 
-// u [B][r], then (matrix-core predictor, B >= 16) the K-slice partials of x P1
+// u [B][r], then (matrix-core predictor, B >= 2) the per-token u scales [B]
+// and the K-slice partials of x P1
 size_t ws_pred_bytes(int r, int B) {
     size_t v = WS_CTR_BYTES + align256((size_t)B * r * 4);
-    if (B >= MFMA_MIN_BATCH) v += align256((size_t)P1_KS * B * r * 4);
+    if (B >= MFMA_MIN_BATCH) v += align256((size_t)B * 4) + align256((size_t)P1_KS * B * r * 4);
     return v;
 }
 
@@ -252,10 +253,14 @@ pi_status launch_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
     const size_t xbytes = (size_t)BT * a.d * (XT == F32 ? 4 : 2);
     const size_t words = a.mask ? (size_t)(a.n + 63) / 64 : 0;
     const size_t mbytes = words ? words * 8 + (words + 1) * 4 : 0;   // mask words + their scan
-    if (xbytes <= XLDS_MAX)
-        return launch(PI_K_UP, k_up<WT, XT, BT, ACT, true>, dim3(grid), dim3(THREADS),
-                      xbytes + mbytes, s, a);
-    return launch(PI_K_UP, k_up<WT, XT, BT, ACT, false>, dim3(grid), dim3(THREADS), mbytes, s, a);
+    if (xbytes <= XLDS_MAX) {
+        auto kern = k_up<WT, XT, BT, ACT, true>;
+        TRY(allow_lds(kern, xbytes + mbytes));
+        return launch(PI_K_UP, kern, dim3(grid), dim3(THREADS), xbytes + mbytes, s, a);
+    }
+    auto kern = k_up<WT, XT, BT, ACT, false>;
+    TRY(allow_lds(kern, mbytes));
+    return launch(PI_K_UP, kern, dim3(grid), dim3(THREADS), mbytes, s, a);
 }
 
 // chunk partials -> y_hot, y_cold, y (one thread per 4 consecutive outputs)
@@ -308,12 +313,16 @@ pi_status launch_fused(const FfnArgs& a, const DownOut& o, hipStream_t s) {
                   dim3(RE * RS), 0, s, a, o);
 }
 
+// Only the (chunks per thread, batch tile) pairs use_fused admits are
+// instantiated: four chunks per thread at batch 1 with f32 / f16 weights.
 template <int WT, int XT, int BT, int ACT>
 pi_status fused_nc_dispatch(const FfnArgs& a, const DownOut& o, hipStream_t s) {
     switch (fused_nc(a.d, WT)) {
     case 1: return launch_fused<WT, XT, BT, ACT, 1>(a, o, s);
     case 2: return launch_fused<WT, XT, BT, ACT, 2>(a, o, s);
-    default: return launch_fused<WT, XT, BT, ACT, 4>(a, o, s);
+    default:
+        if constexpr (BT == 1 && WT != Q4) return launch_fused<WT, XT, BT, ACT, 4>(a, o, s);
+        return fail(PI_ERR_SHAPE, "fused kernel: row too wide for this batch");
     }
 }
 
@@ -509,7 +518,7 @@ const char* pi_last_error(void) { return g_err; }
 const char* pi_kernel_name(int32_t kid) {
     static const char* names[PI_K_COUNT] = {"k_pred_l1", "k_pred_l2", "k_compact", "k_up", "k_down",
                                             "k_merge", "k_profile", "k_index", "k_copy", "k_reduce",
-                                            "k_ffn", "k_accumulate_mask"};
+                                            "k_ffn", "k_accumulate_mask", "k_stream_read"};
     return (kid >= 0 && kid < PI_K_COUNT) ? names[kid] : "?";
 }
 
@@ -570,19 +579,19 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
     const int wt = p->wdtype;
     if (B >= MFMA_MIN_BATCH && wt == F16 && xdtype == F16 && p->r % KS == 0 && p->d % KS == 0) {
         // matrix-core predictor: K-split first layer, slice sum + ReLU, second layer
-        float* part = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * p->r * 4));
+        float* uscale = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * p->r * 4));
+        float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(uscale) + align256((size_t)B * 4));
         const dim3 g1((p->r + P1_ROWS - 1) / P1_ROWS, P1_KS);
         const int mt = mfma_mt(B);
         auto pred1 = mt == 1 ? k_mfma_pred1<1> : mt == 2 ? k_mfma_pred1<2> : k_mfma_pred1<4>;
         TRY(launch(PI_K_PRED_L1, pred1, g1, dim3(MFMA_WG), 0, s, (const uint8_t*)p->P1t,
                    (const uint8_t*)x, p->d, p->r, B, part));
-        const int64_t len = (int64_t)B * p->r;
-        int grid = (int)((len / 4 + THREADS - 1) / THREADS);
-        if (grid > 1024) grid = 1024;
-        TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(grid), dim3(THREADS), 0, s, (const float*)part, len, u));
+        TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(B), dim3(THREADS), 0, s, (const float*)part, B, p->r,
+                   u, uscale));
         auto pred2 = mt == 1 ? k_mfma_pred2<1> : mt == 2 ? k_mfma_pred2<2> : k_mfma_pred2<4>;
         TRY(launch(PI_K_PRED_L2, pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
-                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, p->n, p->r, B, mask, logits));
+                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, (const float*)uscale,
+                   p->n, p->r, B, mask, logits));
     } else {
         pi_status st;
         if (wt == F32)
@@ -718,6 +727,15 @@ pi_status pi_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (grid > 8192) grid = 8192;
     return launch(PI_K_COPY, k_copy, dim3((unsigned)grid), dim3(THREADS), 0, (hipStream_t)stream,
                   (const u4*)src, (u4*)dst, n16);
+}
+
+pi_status pi_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+    CHECK(bytes >= 0 && bytes % 16 == 0, PI_ERR_SHAPE, "bytes must be a multiple of 16");
+    CHECK(sink && aligned(sink, 4), PI_ERR_ARG, "sink required (4-byte aligned)");
+    CHECK(bytes == 0 || (src && aligned(src, 16)), PI_ERR_ALIGN, "src must be 16-byte aligned");
+    const int64_t n16 = bytes / 16;
+    return launch(PI_K_STREAM, k_stream_read, dim3(STREAM_WG), dim3(THREADS), 0, (hipStream_t)stream,
+                  (const u4*)src, n16, sink);
 }
 
 pi_status pi_kernel_timer_start(int32_t kid, int32_t max_launches) {

@@ -110,6 +110,9 @@ template <> struct Dot<F16, F32> {
 // Q4_0 block: code byte t holds element t (low nibble) and t + 16 (high nibble).
 // Two codes go into one half2 as 1024 + q (exponent 10, so the integer is exact),
 // and subtracting 1032 leaves q - 8 exactly; v_dot2 then takes two products.
+// This integer-to-half conversion by OR-ing codes into the mantissa of a
+// power-of-two constant is the published "magic number" method for 4-bit
+// weights (Kim et al., arXiv 2211.10017, fast int4-to-fp16 conversion).
 __device__ __forceinline__ h2 q4_pair(unsigned two_bytes_in_halves) {
     h2 v = bits_h2((two_bytes_in_halves & 0x000F000Fu) | 0x64006400u);
     return v - h2{(_Float16)1032.0f, (_Float16)1032.0f};
@@ -174,6 +177,8 @@ template <> struct Down<F32> {
         acc[2] = fmaf(h, bits_f(w.z), acc[2]);
         acc[3] = fmaf(h, bits_f(w.w), acc[3]);
     }
+    // a value whose axpy adds exact zeros whatever h is
+    __device__ static raw zero() { return u4{0u, 0u, 0u, 0u}; }
     // column of accumulator e, relative to the lane's first column
     __device__ static int col(int e) { return e; }
 };
@@ -195,6 +200,7 @@ template <> struct Down<F16> {
         acc[6] = fmaf(h, half_lo(w.w), acc[6]);
         acc[7] = fmaf(h, half_hi(w.w), acc[7]);
     }
+    __device__ static raw zero() { return u4{0u, 0u, 0u, 0u}; }
     __device__ static int col(int e) { return e; }
 };
 
@@ -221,6 +227,13 @@ template <> struct Down<Q4> {
             acc[t] = fmaf(hs, (float)(int)(byte & 15u) - 8.0f, acc[t]);
             acc[8 + t] = fmaf(hs, (float)(int)(byte >> 4) - 8.0f, acc[8 + t]);
         }
+    }
+    // codes of 8 (weight 0) with a zero scale
+    __device__ static raw zero() {
+        Q4Half r;
+        r.codes = u2{0x88888888u, 0x88888888u};
+        r.scale = 0.0f;
+        return r;
     }
     // accumulators 0..7 -> columns k0..k0+7, 8..15 -> columns k0+16..k0+23
     __device__ static int col(int e) { return e < 8 ? e : e + 8; }

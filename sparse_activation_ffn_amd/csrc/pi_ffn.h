@@ -84,7 +84,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     // 3 matrices each) plus BT x NC x EPC accumulators must fit in 256 VGPRs.
     // Two buffers of G2 rows, or, where it holds more rows without spilling,
     // three buffers of G3 rows (a group's loads are then issued two groups ahead)
-    constexpr int G0 = (WT == Q4 ? 4 : 8) / NC / (ACT == REGLU ? 2 : 1) / (BT >= 4 ? 2 : 1);
+    constexpr int G0 = (WT == Q4 ? 4 : 8) / NC / (ACT == REGLU ? 2 : 1) / (BT >= 2 ? 2 : 1);
     constexpr int G2 = G0 > 0 ? G0 : 1;
     constexpr int G3 = (2 * G2 + 2) / 3;
     constexpr bool RING3 = BT == 1 && NC <= (WT == Q4 ? 1 : 2) && 3 * G3 > 2 * G2;
@@ -359,12 +359,17 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         if (r < 0 || b >= nb) hv = 0.0f;
 #pragma unroll
                         for (int k = 0; k < NC; ++k) {
+                            // a slot that holds no row read row 0 of the partition
+                            // (clamped, unconditional loads): its weights are replaced by
+                            // zeros here, where they are consumed, so a non-finite value
+                            // in a row outside the active set never reaches y
                             if (WT == Q4) {
-                                const float hs = hv * half_f(R.sd[g][k]);
+                                const float hs = r >= 0 ? hv * half_f(R.sd[g][k]) : 0.0f;
                                 hsum[b][k] += hs;
                                 Axpy<WT>::run(R.wd[g][k], 0.f, hs, acc[b][k]);
                             } else {
-                                Axpy<WT>::run(R.wd[g][k], 0.f, hv, acc[b][k]);
+                                const u4 wd = r >= 0 ? R.wd[g][k] : u4{0u, 0u, 0u, 0u};
+                                Axpy<WT>::run(wd, 0.f, hv, acc[b][k]);
                             }
                         }
                     }

@@ -559,9 +559,9 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
             const int len = min(STAGE, hi - s0);
             __syncthreads();                  // the previous stage is consumed
             for (int t = threadIdx.x; t < len; t += THREADS) {
-                int row = idx ? idx[s0 + t] : s0 + t;
-                if ((unsigned)row >= (unsigned)prow_max) row = 0;   // k_up gave it h = 0
-                s_row[t] = row;
+                const int row = idx ? idx[s0 + t] : s0 + t;
+                // an id outside the partition (k_up gave it h = 0) is not read at all
+                s_row[t] = (unsigned)row < (unsigned)prow_max ? row : -1;
 #pragma unroll
                 for (int b = 0; b < BT; ++b)
                     s_h[b][t] = b0 + b < B ? a.h[(int64_t)(b0 + b) * a.h_ld + hbase + s0 + t] : 0.f;
@@ -577,13 +577,18 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
 #pragma unroll
                 for (int q = 0; q < U; ++q) {
                     const int row = __builtin_amdgcn_readfirstlane(s_row[tq[q]]);
-                    w[q] = D::load(base + (int64_t)row * a.rb, a.d, colL);
+                    w[q] = D::load(base + (int64_t)max(row, 0) * a.rb, a.d, colL);
                 }
 #pragma unroll
                 for (int q = 0; q < U; ++q) {
-                    const bool valid = t0 + NWAVES * q < len;
+                    // slots past the stage and ids that are not rows take zero weights
+                    // (replaced here, where they are consumed), so only listed rows
+                    // of the partition contribute, and a non-finite value in any
+                    // other row never reaches y
+                    const bool valid = t0 + NWAVES * q < len && s_row[tq[q]] >= 0;
+                    const typename D::raw wq = valid ? w[q] : D::zero();
 #pragma unroll
-                    for (int b = 0; b < BT; ++b) D::axpy(w[q], valid ? s_h[b][tq[q]] : 0.0f, acc[b]);
+                    for (int b = 0; b < BT; ++b) D::axpy(wq, valid ? s_h[b][tq[q]] : 0.0f, acc[b]);
                 }
             }
         }
@@ -752,6 +757,40 @@ __global__ __launch_bounds__(THREADS) void k_copy(const u4* __restrict__ src, u4
     const int64_t stride = (int64_t)gridDim.x * THREADS;
     for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n16; i += stride)
         dst[i] = src[i];
+}
+
+// Plain read stream (the attainable-bandwidth ceiling for weight streams):
+// reads n16 16-byte words with non-temporal loads, U loads in flight per thread,
+// and stores one xor of them per workgroup so the loads cannot be dropped.
+constexpr int STREAM_WG = 2048;      // workgroups of k_stream_read (8 per compute unit)
+__global__ __launch_bounds__(THREADS) void k_stream_read(const u4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    constexpr int U = 4;
+    __shared__ unsigned s_x[NWAVES];
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u4 v[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) v[q] = ld16_stream(src + i + q * stride);
+#pragma unroll
+        for (int q = 0; q < U; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+    }
+    for (; i < n16; i += stride) {
+        const u4 v = ld16_stream(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, o, WAVE);
+    if ((threadIdx.x & (WAVE - 1)) == 0) s_x[threadIdx.x / WAVE] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned t = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) t ^= s_x[w];
+        sink[blockIdx.x] = t;
+    }
 }
 
 __global__ __launch_bounds__(THREADS) void k_zero(u4* __restrict__ dst, int64_t n16) {

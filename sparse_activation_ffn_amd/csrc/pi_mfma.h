@@ -47,7 +47,8 @@ __device__ __forceinline__ f4m mfma32(h8 a, h8 b, f4m c) {
 }
 
 // Two 4-bit codes (bits 0..3 and 16..19 of v) -> two f16 values (q - 8) * s,
-// each rounded once: 0x6400 | q is the f16 1024 + q, and 1024 + q - 1032 is exact.
+// each rounded once: 0x6400 | q is the f16 1024 + q, and 1024 + q - 1032 is exact
+// (the "magic number" int4-to-fp16 conversion of Kim et al., arXiv 2211.10017).
 __device__ __forceinline__ unsigned q4_pair(unsigned v, h2v s2) {
     const unsigned bits = (v & 0x000f000fu) | 0x64006400u;
     h2v t = __builtin_bit_cast(h2v, bits);
@@ -696,38 +697,70 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred1(const uint8_t* __restric
     }
 }
 
-// u = ReLU(sum of the P1_KS slice partials, in slice order); 4 outputs per thread.
-__global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ part, int64_t len,
-                                                    float* __restrict__ u) {
-    const int64_t len4 = len / 4;
-    const f4* P = reinterpret_cast<const f4*>(part);
-    for (int64_t t = (int64_t)blockIdx.x * THREADS + threadIdx.x; t < len4; t += (int64_t)gridDim.x * THREADS) {
-        f4 v[P1_KS];
+// u = ReLU(sum of the P1_KS slice partials, in slice order), one workgroup per
+// token (r <= 4096: at most 16 values per thread).  The workgroup also finds the
+// token's largest u and writes the power of two uscale[b] = 2^(14 - e), e =
+// floor(log2(max u)), that maps that maximum into [2^14, 2^15): the second
+// layer splits u * uscale into two f16 parts, and the power of two keeps the
+// high part finite and normal whatever the magnitude of u (u itself is stored
+// unscaled, fp32).
+constexpr int UR_MAX = 16;      // u values per thread of k_u_relu (r <= 16 * 256)
+__global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ part, int B, int r,
+                                                    float* __restrict__ u, float* __restrict__ uscale) {
+    __shared__ float s_max[NWAVES];
+    const int b = blockIdx.x;
+    const int64_t len = (int64_t)B * r;
+    float vmax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < P1_KS; ++k) v[k] = P[k * len4 + t];
-        f4 sum = v[0];
+    for (int t = 0; t < UR_MAX; ++t) {
+        const int j = threadIdx.x + THREADS * t;
+        if (j < r) {
+            const int64_t at = (int64_t)b * r + j;
+            float v[P1_KS];
 #pragma unroll
-        for (int k = 1; k < P1_KS; ++k) {
-            sum.x += v[k].x; sum.y += v[k].y; sum.z += v[k].z; sum.w += v[k].w;
+            for (int k = 0; k < P1_KS; ++k) v[k] = part[k * len + at];
+            float sum = v[0];
+#pragma unroll
+            for (int k = 1; k < P1_KS; ++k) sum += v[k];
+            const float uv = sum > 0.0f ? sum : 0.0f;
+            u[at] = uv;
+            vmax = fmaxf(vmax, uv);
         }
-        reinterpret_cast<f4*>(u)[t] = f4{sum.x > 0.f ? sum.x : 0.f, sum.y > 0.f ? sum.y : 0.f,
-                                         sum.z > 0.f ? sum.z : 0.f, sum.w > 0.f ? sum.w : 0.f};
+    }
+    // largest u of the token (max is exact, so the order does not matter)
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o, WAVE));
+    if ((threadIdx.x & (WAVE - 1)) == 0) s_max[threadIdx.x / WAVE] = vmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = s_max[0];
+#pragma unroll
+        for (int w = 1; w < NWAVES; ++w) m = fmaxf(m, s_max[w]);
+        // m == 0 (every u zero) or not finite: no scaling
+        const int e = (m > 0.0f && m <= 3.0e38f) ? ilogbf(m) : 14;
+        uscale[b] = ldexpf(1.0f, 14 - e);
     }
 }
 
 // ===========================================================================
 // Second layer + threshold + union over tokens: logits = u P2 + b2 on matrix
-// cores, 128 neurons (two mask words) per workgroup.  u is fp32; it enters the
-// matrix cores as the sum of two f16 parts (hi = f16(u), lo = f16(u - hi)),
-// whose products with the f16 weights are exact, so the logits keep fp32
-// accuracy and the threshold decisions match the fp32 path.
+// cores, 128 neurons (two mask words) per workgroup.  u is fp32; per token it is
+// scaled by the power of two uscale[b] (exact) and enters the matrix cores as
+// the sum of two f16 parts, hi = f16(u s) and lo = f16(u s - hi), whose
+// products with the f16 weights are exact in the fp32 accumulation.  hi + lo
+// carries u s to about 22 significant bits (lo is rounded too), so the logits
+// come within ~2^-22 relative of the fp32 path, far inside the 1e-5 decision
+// band; the scale keeps hi finite for any u and keeps hi + lo away from the
+// f16 subnormals for every u above 2^-28 of the token's largest.  The epilogue
+// multiplies the accumulator by 1 / uscale[b] (exact) before adding b2.
 // ===========================================================================
 constexpr int P2_ROWS = 128;    // neurons per workgroup (32 per wave)
 
 template <int MT>
 __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restrict__ P2t,
                                                        const float* __restrict__ b2, float thr,
-                                                       const float* __restrict__ u, int n, int r,
+                                                       const float* __restrict__ u,
+                                                       const float* __restrict__ uscale, int n, int r,
                                                        int B, uint64_t* __restrict__ mask,
                                                        float* __restrict__ logits) {
     constexpr int J = P2_ROWS * 16 / MFMA_WG;         // 16-byte weight loads per thread
@@ -766,6 +799,10 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
             R.uv[j][1] = up[1];
         }
     };
+    // per-token scales of this thread's u pieces (fixed for the whole kernel)
+    float usc[UJ];
+#pragma unroll
+    for (int j = 0; j < UJ; ++j) usc[j] = uscale[min((min(tid + MFMA_WG * j, UN - 1) >> 4), B - 1)];
     auto store = [&](const Stage& R, bool act) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -782,7 +819,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
                 unsigned hw[4], lw[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const float a0 = ok ? v[2 * p] : 0.0f, a1 = ok ? v[2 * p + 1] : 0.0f;
+                    const float a0 = ok ? v[2 * p] * usc[j] : 0.0f, a1 = ok ? v[2 * p + 1] * usc[j] : 0.0f;
                     const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
                     const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
                     hw[p] = (unsigned)__builtin_bit_cast(uint16_t, h0) | ((unsigned)__builtin_bit_cast(uint16_t, h1) << 16);
@@ -829,7 +866,9 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tok = 16 * mt + 4 * q + e;
-                const float lg = acc[jn][mt][e] + bias;
+                // 1 / uscale is a power of two: the product is exact, one rounding in the add
+                const float inv = tok < B ? ldexpf(1.0f, -ilogbf(uscale[tok])) : 1.0f;
+                const float lg = fmaf(acc[jn][mt][e], inv, bias);
                 if (tok < B) {
                     fire |= lg > thr;
                     if (logits && i < n) logits[(int64_t)tok * n + i] = lg;

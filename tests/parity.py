@@ -28,17 +28,19 @@ def mask_bits(words: np.ndarray, n: int) -> np.ndarray:
     return bits[:n].astype(bool), bits[n:]
 
 
-def ambiguous(logits: np.ndarray, thr: float = 0.0) -> np.ndarray:
-    clear_on = (logits > thr + BAND).any(axis=0)
-    near = (np.abs(logits - thr) <= BAND).any(axis=0)
+def ambiguous(logits: np.ndarray, thr: float = 0.0, band: float = BAND) -> np.ndarray:
+    clear_on = (logits > thr + band).any(axis=0)
+    near = (np.abs(logits - thr) <= band).any(axis=0)
     return near & ~clear_on
 
 
-def check_mask(gpu_words, oracle_words, oracle_logits, n, thr=0.0):
+def check_mask(gpu_words, oracle_words, oracle_logits, n, thr=0.0, band=BAND):
+    """`band` is BAND unless a test scales the logits by a known power of two (then
+    the band scales with them)."""
     g, gtail = mask_bits(gpu_words, n)
     o, _ = mask_bits(oracle_words, n)
     assert not gtail.any(), "mask tail bits must be 0"
-    amb = ambiguous(oracle_logits, thr)
+    amb = ambiguous(oracle_logits, thr, band)
     bad = np.flatnonzero((g != o) & ~amb)
     assert bad.size == 0, f"{bad.size} predicted bits differ outside the band, e.g. {bad[:8]}"
     return int(amb.sum())
@@ -80,7 +82,7 @@ def permute_layer(L, perm):
     """Host copy of the layer with per-neuron rows in slot order (plain indexing)."""
     import dataclasses
     take = lambda a: None if a is None else np.ascontiguousarray(a[perm])  # noqa: E731
-    return dataclasses.replace(L, p=L.p[perm], W_up=take(L.W_up), W_gate=take(L.W_gate),
+    return dataclasses.replace(L, p=take(L.p), W_up=take(L.W_up), W_gate=take(L.W_gate),
                                W_downT=take(L.W_downT), b_up=take(L.b_up), b_gate=take(L.b_gate),
                                P2t=take(L.P2t), b2=take(L.b2))
 
@@ -95,3 +97,17 @@ def oracle_ffn(Lh, n_hot, x, hot_idx, cold_idx):
     else:
         y_cold = None
     return y_hot, y_cold, O.merge(y_hot, y_cold)
+
+
+def oracle_threads():
+    """Threads for the oracle's outer loops in the GPU tests (results are bit-identical
+    for any count): the cores this process may use, at most 16."""
+    import os
+    try:
+        k = len(os.sched_getaffinity(0))
+    except AttributeError:
+        k = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        k = min(k, int(env))
+    return max(1, min(16, k))

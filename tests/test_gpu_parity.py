@@ -13,13 +13,22 @@ torch = pytest.importorskip("torch")
 
 from oracle import oracle as O  # noqa: E402
 from parity import (check_close, check_mask, mask_bits, oracle_ffn,  # noqa: E402
-                    permute_layer)
+                    oracle_threads, permute_layer)
 from sparse_activation_ffn_amd import binding as pb  # noqa: E402
 from sparse_activation_ffn_amd.layer import DeviceLayer, StepBuffers  # noqa: E402
 from workload import synth as S  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _threaded_oracle():
+    """The oracle's outer loops on the host's cores (bit-identical results) so the
+    full-size cases finish in seconds."""
+    O.set_threads(oracle_threads())
+    yield
+    O.set_threads(1)
 
 
 def log(*a):
@@ -77,11 +86,15 @@ def check_step(Lh, n_hot, x_np, out, tokens=None):
     return e, namb, len(hot_o) + len(cold_o)
 
 
-def index_layer(L, dl: DeviceLayer, samples: int, rows_checked=None):
-    """Profile on the GPU, check counts, build + check the index, permute on the GPU."""
+def index_layer(L, dl: DeviceLayer, samples: int, rows_checked=None, X=None):
+    """Profile on the GPU, check counts, build + check the index, permute on the GPU.
+    X: the profiling samples as a device tensor (default: drawn on the host)."""
     wl = L.wl
-    X_np = S.make_profile_x(wl, L.layer, samples)
-    X = torch.from_numpy(X_np).to(DEV)
+    if X is None:
+        X_np = S.make_profile_x(wl, L.layer, samples)
+        X = torch.from_numpy(X_np).to(DEV)
+    else:
+        X_np = _np(X)
     counts = dl.profile_counts(X)
     torch.cuda.synchronize()
     cg = _np(counts).astype(np.uint32)
@@ -420,15 +433,15 @@ def test_compact_ignores_tail_bits():
 
 def test_opt30b_full_with_index():
     """OPT-30B-shaped layer (d 7168, n 28672, rank 1024, fp16), 26% hot partition from
-    1024 profiling samples, split + merge, three decode steps."""
+    1024 profiling samples, split + merge, eight decode steps."""
     wl = S.WORKLOADS["opt30b-fp16"]
     L = S.make_layer(wl)
     dl = DeviceLayer.upload(L, DEV)
-    rows = np.random.default_rng(0).choice(wl.n, 48, replace=False)
+    rows = np.random.default_rng(0).choice(wl.n, 256, replace=False)
     Lh, n_hot = index_layer(L, dl, wl.profile_samples, rows_checked=rows)
     assert n_hot == 7454
     buf = StepBuffers(dl, 1, DEV)
-    for step in range(3):
+    for step in range(8):
         x = S.make_x(wl, 0, step, 1)
         e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x))
         log(f"  opt30b step {step}: active {na} (hot {int(buf.counts[0])}), ambiguous {namb}, "
@@ -447,46 +460,68 @@ def test_reglu70b_full(B):
         log(f"  reglu70b B={B} step {step}: union active {na}, ambiguous {namb}, err {e:.2e}")
 
 
-def test_falcon40b_layer_full():
-    """Last layer of the Falcon-40B-shaped stack: 20% hot partition, two steps."""
+@pytest.mark.parametrize("layer", [0, 29, 59])
+def test_falcon40b_layer_full(layer):
+    """Layers 0, 29 and 59 of the Falcon-40B-shaped stack (host-drawn from their
+    seeds): 20% hot partition from 1024 profiling samples, 16 decode steps spread over
+    the 128 (fresh x per step and layer)."""
     wl = S.WORKLOADS["falcon40b-stack-fp16"]
-    L = S.make_layer(wl, layer=59)
+    L = S.make_layer(wl, layer=layer)
     dl = DeviceLayer.upload(L, DEV)
-    rows = np.random.default_rng(1).choice(wl.n, 32, replace=False)
+    rows = np.random.default_rng(1 + layer).choice(wl.n, 64, replace=False)
     Lh, n_hot = index_layer(L, dl, wl.profile_samples, rows_checked=rows)
     assert n_hot == 6553
     buf = StepBuffers(dl, 1, DEV)
-    for step in (0, 127):
-        x = S.make_x(wl, 59, step, 1)
-        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x))
-        log(f"  falcon layer 59 step {step}: active {na}, err {e:.2e}")
+    worst = 0.0
+    for step in range(0, 128, 8):
+        x = S.make_x(wl, layer, step, 1)
+        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step % 16 == 0)))
+        worst = max(worst, e)
+    log(f"  falcon layer {layer}: 16 steps, last active {na}, worst err {worst:.2e}")
+
+
+def test_falcon40b_device_drawn_layer():
+    """A layer drawn on the GPU the way the stack benchmark draws its 60 layers
+    (workload.synth.make_layer_device, device-drawn profiling samples and inputs),
+    copied to the host and checked step by step against the oracle: the values the
+    benchmark times."""
+    wl = S.WORKLOADS["falcon40b-stack-fp16"]
+    li = 29
+    t = S.make_layer_device(wl, li, DEV)
+    host = {k: (None if v is None or isinstance(v, float) else _np(v)) for k, v in t.items()}
+    L = S.Layer(wl, li, None, host["W_up"], host["W_gate"], host["W_downT"], host["b_up"],
+                host["b_gate"], host["P1t"], host["P2t"], host["b2"], 0.0)
+    dl = DeviceLayer.from_tensors(wl, t)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(S.SEED + 7 * li + 1)
+    X = torch.randn(wl.profile_samples, wl.d, generator=g, device=DEV).to(torch.float16)
+    rows = np.random.default_rng(7).choice(wl.n, 64, replace=False)
+    Lh, n_hot = index_layer(L, dl, wl.profile_samples, rows_checked=rows, X=X)
+    assert n_hot == 6553
+    del X
+    buf = StepBuffers(dl, 1, DEV)
+    gx = torch.Generator(device=DEV)
+    gx.manual_seed(S.SEED + 99)
+    xs = torch.randn(16, 1, wl.d, generator=gx, device=DEV).to(torch.float16)
+    worst = 0.0
+    for step in range(16):
+        x = _np(xs[step])
+        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step % 2 == 0)))
+        worst = max(worst, e)
+    log(f"  device-drawn falcon layer {li}: 16 steps, last active {na}, worst err {worst:.2e}")
 
 
 @pytest.mark.parametrize("B", [1, 8, 64])
 def test_opt175b_q4_full(B):
+    """OPT-175B-shaped Q4_0 layer: the union mask of all B tokens against the oracle's
+    predictor (ambiguity band), the list bit-exact, the FFN on up to four tokens over
+    the GPU's union list."""
     wl = S.WORKLOADS["opt175b-q4_0"]
     L = S.make_layer(wl)
     dl = DeviceLayer.upload(L, DEV)
     buf = StepBuffers(dl, B, DEV)
     x = S.make_x(wl, 0, 0, B)
-    out = run_step(dl, buf, x, logits=(B == 1))
-    if B < 64:
-        e, namb, na = check_step(L, wl.n, x, out, tokens=None if B == 1 else [0, B - 1])
-    else:
-        # union over 64 tokens: equals the OR of the GPU's single-token masks (checked for all
-        # tokens); two single-token masks are checked against the oracle; the FFN is checked on
-        # two tokens with the GPU's union list
-        acc = np.zeros_like(out["mask"])
-        one = StepBuffers(dl, 1, DEV)
-        for b in range(B):
-            o1 = run_step(dl, one, x[b:b + 1], logits=(b in (0, 63)), partials=False)
-            acc |= o1["mask"]
-            if b in (0, 63):
-                check_step(L, wl.n, x[b:b + 1], o1)
-        assert np.array_equal(acc, out["mask"])
-        hot_o, _ = O.compact(out["mask"], wl.n, wl.n)
-        assert np.array_equal(out["hot"], hot_o)
-        _, _, y = oracle_ffn(L, wl.n, x[[0, 63]], hot_o, np.zeros(0, np.int32))
-        e = check_close(out["y"][[0, 63]], y, "q4_0")
-        na = len(hot_o)
-    log(f"  q4_0 B={B}: union active {na}, err {e:.2e}")
+    out = run_step(dl, buf, x)
+    tokens = None if B == 1 else sorted({0, B // 3, (2 * B) // 3, B - 1})
+    e, namb, na = check_step(L, wl.n, x, out, tokens=tokens)
+    log(f"  q4_0 B={B}: union active {na}, ambiguous {namb}, err {e:.2e}")

@@ -226,3 +226,28 @@ def test_layer_step_composes_the_steps():
     h2, c2 = O.compact(m2, wl.n, n_hot)
     assert np.array_equal(h, h2) and np.array_equal(c, c2)
     assert np.array_equal(y, O.merge(O.sparse_ffn(hot, x, h2), O.sparse_ffn(cold, x, c2)))
+
+
+def test_threaded_oracle_is_bit_identical():
+    """The oracle's outer loops shared among threads (for timing on all host cores)
+    give bit-identical results: each output is still computed by one thread with the
+    same operations in the same order."""
+    wl = S.WORKLOADS["opt175b-q4_0"].scaled(d=512, n=700, r=48, act="reglu")
+    L = S.make_layer(wl)
+    x = S.make_x(wl, 0, 1, 3)
+    part = O.Part.from_layer(L)
+    idx = np.arange(0, wl.n, 3, dtype=np.int32)
+    X = S.make_profile_x(wl, 0, 40)
+    runs = []
+    try:
+        for k in (1, 5):
+            O.set_threads(k)
+            assert O.get_threads() == k
+            m, lg, m32 = O.predict(L.P1t, L.P2t, L.b2, x)
+            y = O.sparse_ffn(part, x, idx)
+            c, c32, amb = O.profile_counts(part, X, band=1e-4)
+            runs.append((m, lg, m32, y, c, c32, amb))
+    finally:
+        O.set_threads(1)
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
