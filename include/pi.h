@@ -197,6 +197,30 @@ pi_status pi_sparse_ffn_split(const pi_ffn_part* hot, const pi_ffn_part* cold, c
                               void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and results as pi_sparse_ffn_split, with no workspace
+ * argument.  Its scratch (h and the fp32 partials of y) lives in a static
+ * device array of PI_SCRATCH_BYTES bytes inside the library; each GPU the
+ * library runs on holds its own copy of it until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *  - Calls whose scratch need (what pi_workspace_bytes gives for these
+ *    shapes) exceeds PI_SCRATCH_BYTES fail with PI_ERR_WORKSPACE and enqueue
+ *    nothing.  The five workload shapes of the library's tests fit.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (no call needs it to start at any value).  Calls that may
+ *    overlap on one GPU (different streams, or host threads without ordering)
+ *    race on it and must be ordered by the caller.
+ *  - `stream` must belong to the current device (PI_ERR_ARG otherwise).  The
+ *    first call on a device looks up that device's copy of the array.
+ */
+#define PI_SCRATCH_BYTES (32u << 20)
+pi_status pi_sparse_ffn_split_noalloc(const pi_ffn_part* hot, const pi_ffn_part* cold,
+                                      const void* x, int32_t B, int32_t xdtype,
+                                      const uint64_t* mask, const pi_active_lists* lists,
+                                      float* y_hot, float* y_cold, float* y, void* stream);
+
+/*
  * Merge of two partial outputs (CSDN article, hybrid-design figure: the
  * partitions' results are combined on the GPU): y = y_hot + y_cold, [B][d]
  * float32; y_cold NULL means zeros; y may alias y_hot or y_cold.

@@ -23,10 +23,12 @@ PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
  PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_STREAM, PI_K_COUNT) = range(14)
 PI_STREAM_SINK_WORDS = 2048
+PI_SCRATCH_BYTES = 32 << 20
 
 # every symbol include/pi.h declares
 EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_active",
-           "pi_sparse_ffn", "pi_sparse_ffn_split", "pi_merge", "pi_dense_ffn",
+           "pi_sparse_ffn", "pi_sparse_ffn_split", "pi_sparse_ffn_split_noalloc", "pi_merge",
+           "pi_dense_ffn",
            "pi_profile_counts", "pi_build_neuron_index", "pi_accumulate_mask", "pi_permute_rows",
            "pi_copy", "pi_stream_read",
            "pi_kernel_timer_start", "pi_kernel_timer_stop", "pi_kernel_name", "pi_status_string",
@@ -76,6 +78,7 @@ def lib() -> C.CDLL:
         "pi_compact_active": ([P, I32, P, P], I32),
         "pi_sparse_ffn": ([P, P, I32, I32, P, P, P, P, SZ, P], I32),
         "pi_sparse_ffn_split": ([P, P, P, I32, I32, P, P, P, P, P, P, SZ, P], I32),
+        "pi_sparse_ffn_split_noalloc": ([P, P, P, I32, I32, P, P, P, P, P, P], I32),
         "pi_merge": ([P, P, I32, I32, P, P], I32),
         "pi_dense_ffn": ([P, P, I32, I32, P, P, SZ, P], I32),
         "pi_profile_counts": ([P, P, I32, I32, P, P], I32),
@@ -168,6 +171,15 @@ def pi_sparse_ffn_split(hot: FfnPart, cold: Optional[FfnPart], x, lists: ActiveL
                                      ptr(y_hot), ptr(y_cold), ptr(y), ptr(ws),
                                      0 if ws is None else ws.numel() * ws.element_size(),
                                      stream_handle(stream)))
+
+
+def pi_sparse_ffn_split_noalloc(hot: FfnPart, cold: Optional[FfnPart], x, lists: ActiveLists,
+                                y_hot=None, y_cold=None, y=None, stream=None, mask=None):
+    """pi_sparse_ffn_split with the library's static scratch instead of a workspace."""
+    _check(lib().pi_sparse_ffn_split_noalloc(C.byref(hot), None if cold is None else C.byref(cold),
+                                             ptr(x), x.shape[0], dtype_code(x), ptr(mask),
+                                             C.byref(lists), ptr(y_hot), ptr(y_cold), ptr(y),
+                                             stream_handle(stream)))
 
 
 def pi_merge(y_hot, y_cold, y, stream=None):

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "pi.h"
@@ -16,6 +17,11 @@
 #include "pi_mfma.h"
 
 using namespace pi;
+
+// Scratch of pi_sparse_ffn_split_noalloc (h and the partials of y), in device
+// memory the library owns: one copy per GPU.  In host code this name is only a
+// stand-in; the device address comes from hipGetSymbolAddress (scratch_ptr).
+static __device__ __align__(256) uint8_t scratch[PI_SCRATCH_BYTES];
 
 namespace {
 
@@ -150,6 +156,38 @@ pi_status launch(int kid, K kernel, dim3 grid, dim3 block, size_t shmem, hipStre
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(PI_ERR_HIP, "%s launch: %s", pi_kernel_name(kid), hipGetErrorString(e));
+    return PI_OK;
+}
+
+// ---- static scratch of the no-allocation entry point ------------------------------
+// `scratch` (file scope, below the includes): one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+pi_status scratch_ptr(hipStream_t s, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PI_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (s) {
+        int sdev = -1;
+        e = hipStreamGetDevice(s, &sdev);
+        if (e != hipSuccess) return fail(PI_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev) return fail(PI_ERR_ARG, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(PI_ERR_HIP, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PI_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return PI_OK;
 }
 
@@ -412,7 +450,7 @@ pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, i
 pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x, int B,
                      int xdtype, const uint64_t* mask, const int32_t* idx0, const int32_t* idx1,
                      const int32_t* counts, bool dense, float* y0, float* y1, float* y, void* ws,
-                     size_t ws_bytes, hipStream_t s) {
+                     size_t ws_bytes, hipStream_t s, bool static_ws = false) {
     TRY(check_part(hot, "hot", !dense));
     const bool has_cold = cold && cold->rows > 0;
     if (cold) TRY(check_part(cold, "cold", true));
@@ -435,6 +473,15 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     const bool mfma = use_mfma(d, wt, xdtype, B);
     const bool fused = !mfma && use_fused(d, wt, xdtype, B);
     const int nch = fused ? NWG_FUSED : mfma ? mfma_chunks(d) : pick_nch(d, wt, B);
+    if (static_ws) {
+        // the no-allocation entry point: the library's own scratch, checked first
+        const size_t need = ws_ffn_bytes(d, n, B, nch);
+        CHECK(need <= (size_t)PI_SCRATCH_BYTES, PI_ERR_WORKSPACE,
+              "these shapes need %zu bytes of scratch; the static scratch holds %zu (PI_SCRATCH_BYTES)",
+              need, (size_t)PI_SCRATCH_BYTES);
+        TRY(scratch_ptr(s, &ws));
+        ws_bytes = PI_SCRATCH_BYTES;
+    }
     TRY(check_ws(ws, ws_bytes, ws_ffn_bytes(d, n, B, nch)));
 
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -637,6 +684,16 @@ pi_status pi_sparse_ffn_split(const pi_ffn_part* hot, const pi_ffn_part* cold, c
     CHECK(hot && lists->n_hot == hot->rows, PI_ERR_SHAPE, "lists->n_hot must equal hot->rows");
     return ffn_common(hot, cold, x, B, xdtype, mask, lists->hot_idx, lists->cold_idx,
                       lists->counts, false, y_hot, y_cold, y, ws, ws_bytes, (hipStream_t)stream);
+}
+
+pi_status pi_sparse_ffn_split_noalloc(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                                      int32_t B, int32_t xdtype, const uint64_t* mask,
+                                      const pi_active_lists* lists, float* y_hot, float* y_cold,
+                                      float* y, void* stream) {
+    CHECK(lists, PI_ERR_ARG, "lists required");
+    CHECK(hot && lists->n_hot == hot->rows, PI_ERR_SHAPE, "lists->n_hot must equal hot->rows");
+    return ffn_common(hot, cold, x, B, xdtype, mask, lists->hot_idx, lists->cold_idx, lists->counts,
+                      false, y_hot, y_cold, y, nullptr, 0, (hipStream_t)stream, true);
 }
 
 pi_status pi_dense_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype, float* y,

@@ -142,3 +142,16 @@ def test_neuron_index_host_side(L):
 def test_timer_validation(L):
     assert L.pi_kernel_timer_start(-1, 4) == pb.PI_ERR_ARG
     assert L.pi_kernel_timer_start(pb.PI_K_UP, 0) == pb.PI_ERR_ARG
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch_on_the_host(L):
+    """The no-allocation entry point checks its static scratch bound before any HIP
+    call: shapes needing more than PI_SCRATCH_BYTES fail with PI_ERR_WORKSPACE."""
+    hot = pb.FfnPart(1024, 262144, pb.PI_F32, pb.PI_RELU, FAKE, None, None, None, FAKE)
+    lists = pb.ActiveLists(262144, FAKE, None, FAKE)
+    rc = L.pi_sparse_ffn_split_noalloc(C.byref(hot), None, FAKE, 64, pb.PI_F32, None,
+                                       C.byref(lists), None, None, FAKE, None)
+    assert rc == pb.PI_ERR_WORKSPACE
+    assert b"static scratch" in L.pi_last_error()
+    assert L.pi_sparse_ffn_split_noalloc(C.byref(hot), None, FAKE, 64, pb.PI_F32, None, None,
+                                         None, None, FAKE, None) == pb.PI_ERR_ARG
