@@ -17,7 +17,7 @@ seeded x per step, so the 256 MB Infinity Cache cannot serve the weights.
 
 Reported on one JSON line: mean microseconds per layer step (`value`, from a
 replay of the timed steps captured in one HIP graph) and its p10/p50/p90 over
-the steps (each step replayed from its own graph between HIP events), the
+the steps (HIP events between eagerly launched steps), the
 achieved GB/s on the bytes the step must touch, per-kernel durations from HIP
 events recorded at each kernel's own dispatch, the roofline of the dominant
 kernel against the 8 TB/s HBM peak and against the attainable read rate of a
@@ -181,21 +181,14 @@ def time_stream(pb, torch, nbytes, dev, launches=16):
     return nbytes / (ms / k * 1e-3) / 1e9
 
 
-def replay_per_step(torch, step, idxs):
-    """Device time of each step replayed from its own graph between HIP events."""
-    graphs = []
-    for i in idxs:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
-    for g in graphs[:2]:
-        g.replay()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+def per_step_us(torch, step, idxs):
+    """Device time of each step: HIP events recorded on the stream between steps
+    launched eagerly (the host enqueues a step faster than the GPU runs one, so the
+    stream never idles between them)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(idxs) + 1)]
     ev[0].record()
-    for g, e in zip(graphs, ev[1:]):
-        g.replay()
+    for i, e in zip(idxs, ev[1:]):
+        step(i)
         e.record()
     torch.cuda.synchronize()
     return np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev[:-1], ev[1:])])
@@ -439,12 +432,12 @@ def main():
     extras = {}
     if not args.no_extras:
         log("[bench] per-step graphs, stream ceiling, literal predictor ...")
-        per = replay_per_step(torch, step, list(range(W, W + K)))
+        per = per_step_us(torch, step, list(range(W, W + K)))
         extras["step_us_percentiles"] = {
             "p10": round(float(np.percentile(per, 10)), 3),
             "p50": round(float(np.percentile(per, 50)), 3),
             "p90": round(float(np.percentile(per, 90)), 3),
-            "how": "each timed step replayed from its own HIP graph between HIP events"}
+            "how": "HIP events between eagerly launched steps"}
         att = time_stream(pb, torch, int(kb_mean[dom]), dev)
         att_long = time_stream(pb, torch, STREAM_BUF_BYTES // 2, dev, launches=8)
         roofline["attainable"] = round(att, 1)
