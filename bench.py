@@ -161,13 +161,18 @@ def cpu_baseline(wl, L, n_hot, B, budget_s=8.0):
             "single_thread_us": round(one_us, 1), "nproc": nproc, "cpu_model": model}
 
 
-def time_stream(pb, torch, nbytes, dev, launches=16):
+def time_stream(pb, torch, nbytes, dev, launches=16, host=False):
     """Attainable read rate of a plain stream of nbytes (per launch, HIP events at the
     kernel's own dispatch), offsets rotating through a 1 GiB buffer so no launch reads
-    what the previous ones left in the caches."""
+    what the previous ones left in the caches.  host: the buffer is pinned host memory
+    (read by the GPU over the host link), one buffer of 2 * nbytes."""
     nbytes = max(16, nbytes // 16 * 16)
-    total = max(STREAM_BUF_BYTES, 8 * nbytes)
-    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    if host:
+        total = 2 * nbytes
+        buf = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    else:
+        total = max(STREAM_BUF_BYTES, 8 * nbytes)
+        buf = torch.empty(total, dtype=torch.uint8, device=dev)
     sink = torch.empty(pb.PI_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
     slots = max(1, total // nbytes)
     for i in range(2):
@@ -320,6 +325,12 @@ def main():
     ap.add_argument("--cold-host", action="store_true",
                     help="place the cold partition's weight rows in pinned host memory "
                          "(capacity tier), read by the kernels over the host link")
+    ap.add_argument("--auto-split", action="store_true",
+                    help="choose n_hot from the measured read rates of HBM and of pinned host "
+                         "memory and a capacity budget (pi_plan_hot_split) instead of the "
+                         "workload's fixed hot fraction")
+    ap.add_argument("--budget-frac", type=float, default=1.0,
+                    help="--auto-split: HBM capacity budget as a fraction of the layer's FFN bytes")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of a captured HIP graph")
     args = ap.parse_args()
@@ -353,6 +364,26 @@ def main():
         base.apply_index(perm, n_hot)
         perm_np = perm.cpu().numpy()
         del X
+    split = None
+    if args.auto_split:
+        if wl.hot_frac is None:
+            raise SystemExit("--auto-split needs a workload with a neuron index")
+        log("[bench] read rates of HBM and pinned host memory, bandwidth-aware split ...")
+        counts_slot = counts.cpu().numpy().astype(np.uint32)[perm_np]
+        r_h = time_stream(pb, torch, STREAM_BUF_BYTES // 2, dev, launches=8)
+        r_l = time_stream(pb, torch, 256 << 20, dev, launches=4, host=True)
+        bpn = S.bytes_per_neuron(wl)
+        budget = int(args.budget_frac * wl.n * bpn)
+        n_hot = pb.pi_plan_hot_split(counts_slot, budget, bpn, r_h, r_l)
+        base.n_hot = n_hot
+        c_hot = float(counts_slot[:n_hot].sum())
+        c_all = float(counts_slot.sum())
+        split = {"hbm_gbps": round(r_h, 1), "link_gbps": round(r_l, 1), "budget_bytes": budget,
+                 "n_hot": n_hot, "fixed_fraction_n_hot": int(wl.hot_frac * wl.n),
+                 "profiled_activation_share_hot": round(c_hot / max(c_all, 1.0), 5),
+                 "hbm_bytes_saved": (wl.n - n_hot) * bpn,
+                 "rule": "smallest n_hot minimising max(hot counts / hbm rate, cold counts / "
+                         "link rate), capped by the budget"}
     layers = [base] + [base.clone() for _ in range(args.instances - 1)]
     if args.cold_host:
         log("[bench] placing the cold partition in pinned host memory ...")
@@ -532,6 +563,7 @@ def main():
         "cold_bytes_per_step": round(float(np.mean([a - h for a, h in zip(active, hot_active)]))
                                      * ((3 if wl.act == "reglu" else 2) * wrow_bytes(wl) + 4)),
         "kernel_bytes": {k: round(kb_mean[k]) for k in sorted(ran)},
+        "auto_split": split,
         "roofline": roofline, **extras, "dense_ffn": dense, "falcon40b_stack": stack,
         "cpu_baseline": cpu,
     }

@@ -221,6 +221,25 @@ pi_status pi_sparse_ffn_split_noalloc(const pi_ffn_part* hot, const pi_ffn_part*
                                       float* y_hot, float* y_cold, float* y, void* stream);
 
 /*
+ * Prompt-phase crossover between the sparse and the dense FFN (CSDN article,
+ * section on the speed results: the advantage shrinks from input length 1 to
+ * 64, where the batch's union of active neurons covers most of the layer).
+ * The same call as pi_sparse_ffn_split, and the lists and counts it writes or
+ * reads are the same; but when the step's active count (hot + cold, on the
+ * device) is at least dense_from, every row of both partitions is computed
+ * instead of the listed ones: y_hot and y_cold are then the dense FFN's two
+ * partial outputs and y the dense FFN.  The choice is made on the device from
+ * the device counts: no host synchronisation.  dense_from >= 1 (a count no
+ * step reaches, e.g. n + 1, keeps the sparse path; 1 always takes the dense
+ * one).  Takes the two-kernel paths for every batch (the fused batch-1 kernel
+ * does not make the choice).
+ */
+pi_status pi_sparse_ffn_crossover(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                                  int32_t B, int32_t xdtype, const uint64_t* mask,
+                                  const pi_active_lists* lists, int32_t dense_from, float* y_hot,
+                                  float* y_cold, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Merge of two partial outputs (CSDN article, hybrid-design figure: the
  * partitions' results are combined on the GPU): y = y_hot + y_cold, [B][d]
  * float32; y_cold NULL means zeros; y may alias y_hot or y_cold.
@@ -257,6 +276,28 @@ pi_status pi_profile_counts(const pi_ffn_part* part, const void* X, int32_t S, i
 pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budget_bytes,
                                 int64_t bytes_per_neuron, int32_t* perm, int32_t* n_hot,
                                 void* stream);
+
+/*
+ * Hot/cold split from the tiers' read rates and the capacity budget (CSDN
+ * article, overall-architecture section: neurons are placed from their
+ * activation frequencies and the hardware's bandwidth and capacity;
+ * hybrid-design section: the two partitions compute at the same time and
+ * their results are merged).  counts_slot [host] n: activation counts in slot
+ * order (the order pi_build_neuron_index gives: counts descending).  For K
+ * hot slots the per-step read times of the tiers are taken proportional to
+ *   T_hot(K)  = (double)(sum of counts of slots <  K) / hbm_gbps
+ *   T_cold(K) = (double)(sum of counts of slots >= K) / link_gbps
+ * and, since the tiers overlap, a step costs max(T_hot, T_cold).
+ *   n_hot [host] out = min(K*, floor(budget_bytes / bytes_per_neuron), n),
+ *   K* = the smallest K in [0, n] minimising max(T_hot(K), T_cold(K)).
+ * hbm_gbps / link_gbps: measured read rates of the fast and the slow tier
+ * (e.g. pi_stream_read on device memory and on pinned host memory).  Host
+ * computation only; nothing is enqueued.  Errors: PI_ERR_SHAPE (n out of
+ * 0..2^24), PI_ERR_BUDGET, PI_ERR_ARG (rates not positive and finite, NULL).
+ */
+pi_status pi_plan_hot_split(const uint32_t* counts_slot, int32_t n, int64_t budget_bytes,
+                            int64_t bytes_per_neuron, double hbm_gbps, double link_gbps,
+                            int32_t* n_hot);
 
 /*
  * Online activation statistics (hada.io README summary: "recent updates"

@@ -421,6 +421,49 @@ int or_build_neuron_index(const uint32_t* counts, int64_t n, int64_t budget_byte
     return OR_OK;
 }
 
+/*
+ * Hot/cold split from the two tiers' read rates (CSDN article, overall
+ * architecture section: neurons are placed from their activation frequencies
+ * and the hardware's bandwidth and capacity; hybrid-design section: the two
+ * partitions compute at the same time and their results are merged).
+ * counts_slot[s] is the activation count of the neuron in slot s (slots in
+ * index order, counts descending).  With K hot slots, the expected read time
+ * per step of each tier is proportional to
+ *   T_hot(K)  = (sum of counts of slots <  K) / hbm_rate
+ *   T_cold(K) = (sum of counts of slots >= K) / link_rate
+ * (every neuron owns the same bytes, so they cancel).  The tiers run
+ * concurrently, so a step takes about max(T_hot, T_cold):
+ *   K*    = the smallest K in [0, n] that minimises max(T_hot(K), T_cold(K))
+ *   n_hot = min(K*, floor(budget_bytes / bytes_per_neuron), n)
+ */
+int or_plan_hot_split(const uint32_t* counts_slot, int64_t n, int64_t budget_bytes,
+                      int64_t bytes_per_neuron, double hbm_rate, double link_rate, int64_t* n_hot)
+{
+    if (n < 0 || budget_bytes < 0 || bytes_per_neuron <= 0 || !(hbm_rate > 0.0) ||
+        !(link_rate > 0.0))
+        return OR_BAD;
+    int64_t total = 0;
+    for (int64_t s = 0; s < n; ++s)
+        total += counts_slot[s];
+    int64_t best_k = 0;
+    double best = 0.0;
+    int64_t hot = 0;                                   /* sum of counts of slots < K */
+    for (int64_t K = 0; K <= n; ++K) {
+        if (K > 0) hot += counts_slot[K - 1];
+        double t_hot = (double)hot / hbm_rate;
+        double t_cold = (double)(total - hot) / link_rate;
+        double t = t_hot > t_cold ? t_hot : t_cold;
+        if (K == 0 || t < best) {
+            best = t;
+            best_k = K;
+        }
+    }
+    int64_t cap = budget_bytes / bytes_per_neuron;
+    int64_t k = best_k < cap ? best_k : cap;
+    *n_hot = k < n ? k : n;
+    return OR_OK;
+}
+
 /* ---- one whole layer step ---------------------------------------------- */
 
 /*

@@ -63,6 +63,7 @@ def lib():
         _lib.or_merge.restype = None
         _lib.or_profile_counts.argtypes = [P, P, I, I64, P, P, P, D]
         _lib.or_build_neuron_index.argtypes = [P, I64, I64, I64, P, P]
+        _lib.or_plan_hot_split.argtypes = [P, I64, I64, I64, D, D, P]
         _lib.or_layer_step.argtypes = [I64, I64, I64, I, P, P, P, D, P, P, P, I, I64, P, P, P, P,
                                        P]
     return _lib
@@ -226,6 +227,18 @@ def build_neuron_index(counts, budget_bytes, bytes_per_neuron):
     if rc:
         raise ValueError("or_build_neuron_index rejected its arguments")
     return perm[:n].copy(), int(n_hot.value)
+
+
+def plan_hot_split(counts_slot, budget_bytes, bytes_per_neuron, hbm_rate, link_rate):
+    """n_hot from the tiers' read rates and the capacity budget (counts in slot order)."""
+    c = np.ascontiguousarray(counts_slot, dtype=np.uint32)
+    out = C.c_int64(0)
+    rc = lib().or_plan_hot_split(_ptr(c) if c.size else None, c.size, int(budget_bytes),
+                                 int(bytes_per_neuron), float(hbm_rate), float(link_rate),
+                                 C.byref(out))
+    if rc:
+        raise ValueError("or_plan_hot_split rejected its arguments")
+    return int(out.value)
 
 
 def layer_step(P1t, P2t, b2, threshold, hot: Part, cold, x):

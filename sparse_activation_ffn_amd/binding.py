@@ -27,9 +27,11 @@ PI_SCRATCH_BYTES = 32 << 20
 
 # every symbol include/pi.h declares
 EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_active",
-           "pi_sparse_ffn", "pi_sparse_ffn_split", "pi_sparse_ffn_split_noalloc", "pi_merge",
+           "pi_sparse_ffn", "pi_sparse_ffn_split", "pi_sparse_ffn_split_noalloc",
+           "pi_sparse_ffn_crossover", "pi_merge",
            "pi_dense_ffn",
-           "pi_profile_counts", "pi_build_neuron_index", "pi_accumulate_mask", "pi_permute_rows",
+           "pi_profile_counts", "pi_build_neuron_index", "pi_plan_hot_split",
+           "pi_accumulate_mask", "pi_permute_rows",
            "pi_copy", "pi_stream_read",
            "pi_kernel_timer_start", "pi_kernel_timer_stop", "pi_kernel_name", "pi_status_string",
            "pi_last_error")
@@ -79,10 +81,12 @@ def lib() -> C.CDLL:
         "pi_sparse_ffn": ([P, P, I32, I32, P, P, P, P, SZ, P], I32),
         "pi_sparse_ffn_split": ([P, P, P, I32, I32, P, P, P, P, P, P, SZ, P], I32),
         "pi_sparse_ffn_split_noalloc": ([P, P, P, I32, I32, P, P, P, P, P, P], I32),
+        "pi_sparse_ffn_crossover": ([P, P, P, I32, I32, P, P, I32, P, P, P, P, SZ, P], I32),
         "pi_merge": ([P, P, I32, I32, P, P], I32),
         "pi_dense_ffn": ([P, P, I32, I32, P, P, SZ, P], I32),
         "pi_profile_counts": ([P, P, I32, I32, P, P], I32),
         "pi_build_neuron_index": ([P, I32, I64, I64, P, P, P], I32),
+        "pi_plan_hot_split": ([P, I32, I64, I64, C.c_double, C.c_double, P], I32),
         "pi_accumulate_mask": ([P, I32, P, P], I32),
         "pi_permute_rows": ([P, P, P, I32, I64, P], I32),
         "pi_copy": ([P, P, I64, P], I32),
@@ -182,6 +186,19 @@ def pi_sparse_ffn_split_noalloc(hot: FfnPart, cold: Optional[FfnPart], x, lists:
                                              stream_handle(stream)))
 
 
+def pi_sparse_ffn_crossover(hot: FfnPart, cold: Optional[FfnPart], x, lists: ActiveLists,
+                            dense_from: int, y_hot=None, y_cold=None, y=None, ws=None, stream=None,
+                            mask=None):
+    """pi_sparse_ffn_split, but every row is computed when the device active count
+    reaches dense_from (the prompt-phase crossover)."""
+    _check(lib().pi_sparse_ffn_crossover(C.byref(hot), None if cold is None else C.byref(cold),
+                                         ptr(x), x.shape[0], dtype_code(x), ptr(mask),
+                                         C.byref(lists), int(dense_from), ptr(y_hot), ptr(y_cold),
+                                         ptr(y), ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(),
+                                         stream_handle(stream)))
+
+
 def pi_merge(y_hot, y_cold, y, stream=None):
     B, d = y_hot.shape
     _check(lib().pi_merge(ptr(y_hot), ptr(y_cold), B, d, ptr(y), stream_handle(stream)))
@@ -203,6 +220,18 @@ def pi_build_neuron_index(counts, budget_bytes: int, bytes_per_neuron: int, perm
     _check(lib().pi_build_neuron_index(ptr(counts), counts.numel(), int(budget_bytes),
                                        int(bytes_per_neuron), ptr(perm), C.byref(n_hot),
                                        stream_handle(stream)))
+    return int(n_hot.value)
+
+
+def pi_plan_hot_split(counts_slot, budget_bytes: int, bytes_per_neuron: int, hbm_gbps: float,
+                      link_gbps: float) -> int:
+    """counts_slot: host array (numpy uint32) of activation counts in slot order."""
+    import numpy as np
+    c = np.ascontiguousarray(counts_slot, dtype=np.uint32)
+    n_hot = C.c_int32(0)
+    _check(lib().pi_plan_hot_split(c.ctypes.data if c.size else None, c.size, int(budget_bytes),
+                                   int(bytes_per_neuron), float(hbm_gbps), float(link_gbps),
+                                   C.byref(n_hot)))
     return int(n_hot.value)
 
 

@@ -107,11 +107,11 @@ bool use_mfma(int d, int wt, int xt, int B) {
     return B >= MFMA_MIN_BATCH && B <= MM && xt == F16 && (wt == F16 || wt == Q4) && d % DC == 0;
 }
 // split-K chunks of the matrix-core down kernel: about two workgroups per
-// compute unit
+// compute unit, a multiple of the 8 XCDs (each XCD takes whole chunks)
 int mfma_chunks(int d) {
     const int tiles = d / DC;
-    const int k = 512 / (tiles > 0 ? tiles : 1);
-    return k < 2 ? 2 : k > NCH_MAX ? NCH_MAX : k;
+    const int k = (512 / (tiles > 0 ? tiles : 1) + NXCD - 1) / NXCD * NXCD;
+    return k < NXCD ? NXCD : k > NCH_MAX ? NCH_MAX : k;
 }
 
 // u [B][r], then (matrix-core predictor, B >= 2) the per-token u scales [B]
@@ -416,7 +416,8 @@ pi_status mfma_up_mt(const FfnArgs& a, int rows_cap, hipStream_t s) {
 
 template <int WT, bool LISTS, int MT>
 pi_status mfma_down(const FfnArgs& a, const DownOut& o, hipStream_t s) {
-    return launch(PI_K_DOWN, k_mfma_down<WT, LISTS, MT>, dim3(a.d / DC, o.nch), dim3(DOWN_WG), 0, s, a,
+    // one linear grid: chunk = (id % 8) + 8 m, column tile = (id / 8) % tiles (see the kernel)
+    return launch(PI_K_DOWN, k_mfma_down<WT, LISTS, MT>, dim3((a.d / DC) * o.nch), dim3(DOWN_WG), 0, s, a,
                   o, (const _Float16*)a.h);
 }
 
@@ -450,7 +451,7 @@ pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, i
 pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x, int B,
                      int xdtype, const uint64_t* mask, const int32_t* idx0, const int32_t* idx1,
                      const int32_t* counts, bool dense, float* y0, float* y1, float* y, void* ws,
-                     size_t ws_bytes, hipStream_t s, bool static_ws = false) {
+                     size_t ws_bytes, hipStream_t s, bool static_ws = false, int dense_from = 0) {
     TRY(check_part(hot, "hot", !dense));
     const bool has_cold = cold && cold->rows > 0;
     if (cold) TRY(check_part(cold, "cold", true));
@@ -471,7 +472,9 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     const int d = hot->d, wt = hot->wdtype;
     const int n = hot->rows + (has_cold ? cold->rows : 0);
     const bool mfma = use_mfma(d, wt, xdtype, B);
-    const bool fused = !mfma && use_fused(d, wt, xdtype, B);
+    // the dense crossover is decided on the device by the two-kernel paths; the
+    // fused batch-1 kernel does not take it
+    const bool fused = !mfma && dense_from <= 0 && use_fused(d, wt, xdtype, B);
     const int nch = fused ? NWG_FUSED : mfma ? mfma_chunks(d) : pick_nch(d, wt, B);
     if (static_ws) {
         // the no-allocation entry point: the library's own scratch, checked first
@@ -519,6 +522,7 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
         }
     }
     a.dense_rows = dense ? hot->rows : 0;
+    a.dense_from = dense ? 0 : dense_from;
     a.d = d;
     a.B = B;
     a.rb = row_bytes(wt, d);
@@ -696,6 +700,17 @@ pi_status pi_sparse_ffn_split_noalloc(const pi_ffn_part* hot, const pi_ffn_part*
                       false, y_hot, y_cold, y, nullptr, 0, (hipStream_t)stream, true);
 }
 
+pi_status pi_sparse_ffn_crossover(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                                  int32_t B, int32_t xdtype, const uint64_t* mask,
+                                  const pi_active_lists* lists, int32_t dense_from, float* y_hot,
+                                  float* y_cold, float* y, void* ws, size_t ws_bytes, void* stream) {
+    CHECK(lists, PI_ERR_ARG, "lists required");
+    CHECK(hot && lists->n_hot == hot->rows, PI_ERR_SHAPE, "lists->n_hot must equal hot->rows");
+    CHECK(dense_from >= 1, PI_ERR_ARG, "dense_from must be >= 1");
+    return ffn_common(hot, cold, x, B, xdtype, mask, lists->hot_idx, lists->cold_idx, lists->counts,
+                      false, y_hot, y_cold, y, ws, ws_bytes, (hipStream_t)stream, false, dense_from);
+}
+
 pi_status pi_dense_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype, float* y,
                        void* ws, size_t ws_bytes, void* stream) {
     CHECK(y, PI_ERR_ARG, "y required");
@@ -750,6 +765,37 @@ pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budge
     if (n == 0) return PI_OK;
     return launch(PI_K_INDEX, k_index, dim3((n + THREADS - 1) / THREADS), dim3(THREADS), 0,
                   (hipStream_t)stream, counts, n, perm);
+}
+
+pi_status pi_plan_hot_split(const uint32_t* counts_slot, int32_t n, int64_t budget_bytes,
+                            int64_t bytes_per_neuron, double hbm_gbps, double link_gbps,
+                            int32_t* n_hot) {
+    CHECK(n >= 0 && n <= (1 << 24), PI_ERR_SHAPE, "n must be in 0..2^24");
+    CHECK(budget_bytes >= 0 && bytes_per_neuron > 0, PI_ERR_BUDGET,
+          "budget must be >= 0 and bytes_per_neuron > 0");
+    CHECK(hbm_gbps > 0.0 && link_gbps > 0.0 && hbm_gbps < 1e300 && link_gbps < 1e300, PI_ERR_ARG,
+          "read rates must be positive and finite");
+    CHECK(n_hot && (n == 0 || counts_slot), PI_ERR_ARG, "counts and n_hot required");
+    // expected activations read from each tier per step for every split point K:
+    // hot = counts of slots [0, K), cold = the rest; each tier's read time is its
+    // activations over its rate, and the tiers overlap, so a step costs the larger
+    std::vector<uint64_t> prefix((size_t)n + 1, 0);
+    for (int32_t s = 0; s < n; ++s) prefix[s + 1] = prefix[s] + counts_slot[s];
+    const uint64_t total = prefix[n];
+    int32_t best = 0;
+    double best_t = 0.0;
+    for (int32_t K = 0; K <= n; ++K) {
+        const double t_hot = (double)prefix[K] / hbm_gbps;
+        const double t_cold = (double)(total - prefix[K]) / link_gbps;
+        const double t = std::max(t_hot, t_cold);
+        if (K == 0 || t < best_t) {                  // ties keep the smaller split
+            best_t = t;
+            best = K;
+        }
+    }
+    const int64_t cap = budget_bytes / bytes_per_neuron;
+    *n_hot = (int32_t)std::min<int64_t>(std::min<int64_t>(best, cap), n);
+    return PI_OK;
 }
 
 pi_status pi_accumulate_mask(const uint64_t* mask, int32_t n, uint32_t* counts, void* stream) {

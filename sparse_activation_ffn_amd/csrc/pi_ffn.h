@@ -143,6 +143,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     asm volatile("" ::"s"(a.up[0]), "s"(a.bup[0]), "s"(o.partials), "s"(o.nch));
     store_x(xv0, 0);
     int H, C;
+    bool dense = false;                                // item k is row k (no list)
     int run = 0;                                       // rank of this thread's first set bit
     if (a.mask) {
         // per-thread totals and counts below n_hot (hot ranks are [0, H))
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
             a.out_counts[1] = C;
         }
     } else {
-        item_counts(a, H, C);
+        dense = item_counts(a, H, C);
     }
     int part, lo, hi, nh;
     chunk_range(o.nch, H, C, blockIdx.x, part, lo, hi, nh);
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     const uint8_t* wdn = part == 0 ? a.down[0] : a.down[1];
     const float* bup = part == 0 ? a.bup[0] : a.bup[1];
     const float* bgt = part == 0 ? a.bgate[0] : a.bgate[1];
-    const int32_t* idx = part == 0 ? a.idx[0] : a.idx[1];
+    const int32_t* idx = dense ? nullptr : part == 0 ? a.idx[0] : a.idx[1];
     const int prows = part == 0 ? a.rows[0] : a.rows[1];
     int32_t* const oidx = part == 0 ? a.out_idx[0] : a.out_idx[1];   // (mask mode) list output
 

@@ -259,6 +259,11 @@ struct FfnArgs {
     int n;
     int32_t* out_idx[2];
     int32_t* out_counts;
+    // > 0: when the step's active count (the device counts) reaches dense_from,
+    // every row of both partitions is computed instead of the listed ones (the
+    // prompt-phase crossover to the dense FFN); the lists and counts still
+    // describe the predicted set
+    int dense_from;
 };
 
 // Largest mask (in 64-bit words) whose compaction k_up does in LDS.
@@ -332,24 +337,37 @@ __device__ __forceinline__ int kth_active(const uint64_t* s_words, const int* s_
     return 64 * lo + select_bit(s_words[lo], k - s_scan[lo]);
 }
 
-__device__ __forceinline__ void item_counts(const FfnArgs& a, int& H, int& C) {
+// Whether a predicted set of T active neurons is computed densely (every row).
+__device__ __forceinline__ bool crosses_to_dense(const FfnArgs& a, int T) {
+    return a.dense_from > 0 && T >= a.dense_from;
+}
+
+// Items of the call: H hot, C cold.  Returns true when item k is row k of its
+// partition (dense mode, or the active count reached dense_from), false when
+// items are list entries.
+__device__ __forceinline__ bool item_counts(const FfnArgs& a, int& H, int& C) {
     if (a.counts) {
         // counts beyond the lists' capacities are clamped (never read past a list)
         H = min(max(a.counts[0], 0), a.rows[0]);
         C = a.nparts > 1 ? min(max(a.counts[1], 0), a.rows[1]) : 0;
-    } else {
-        H = a.dense_rows;
-        C = 0;
+        if (!crosses_to_dense(a, H + C)) return false;
+        H = a.rows[0];
+        C = a.nparts > 1 ? a.rows[1] : 0;
+        return true;
     }
+    H = a.dense_rows;
+    C = 0;
+    return true;
 }
 
-__device__ __forceinline__ void item_row(const FfnArgs& a, int item, int H, int& part, int& row) {
+__device__ __forceinline__ void item_row(const FfnArgs& a, int item, int H, bool dense, int& part,
+                                         int& row) {
     if (item < H) {
         part = 0;
-        row = a.idx[0] ? a.idx[0][item] : item;
+        row = dense ? item : a.idx[0][item];
     } else {
         part = 1;
-        row = a.idx[1][item - H];
+        row = dense ? item - H : a.idx[1][item - H];
     }
 }
 
@@ -373,7 +391,8 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int gw = __builtin_amdgcn_readfirstlane((blockIdx.x * THREADS + threadIdx.x) / WAVE);
     const int nw = gridDim.x * NWAVES;
-    int H, C;
+    int H, C, Hm = 0;                         // Hm: hot count of the mask (dense crossover)
+    bool dense = false;
     if (a.mask) {
         // compaction fused here: every workgroup scans the (small) mask in LDS and
         // maps item k to the k-th active id; hot ids (< rows[0]) come first
@@ -390,8 +409,14 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
             a.out_counts[0] = H;
             a.out_counts[1] = C;
         }
+        if (crosses_to_dense(a, T)) {        // the lists are still written below
+            dense = true;
+            Hm = H;
+            H = a.rows[0];
+            C = a.rows[1];
+        }
     } else {
-        item_counts(a, H, C);
+        dense = item_counts(a, H, C);
     }
     const int T = H + C;
     const int nch = a.d / EPC;
@@ -407,15 +432,27 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
             __syncthreads();
         }
         const uint8_t* xg = XLDS ? s_x : a.x + b0 * xrow;
+        if (a.mask && dense && b0 == 0) {
+            // dense crossover: the items are all rows; the lists still name the
+            // predicted set (item k of the mask's ascending order)
+            const int Tm = s_scan[words];
+            for (int k = gw; k < Tm; k += nw) {
+                const int id = kth_active(s_words, s_scan, words, k);
+                if (lane == 0) {
+                    if (k < Hm) a.out_idx[0][k] = id;
+                    else a.out_idx[1][k - Hm] = id - a.rows[0];
+                }
+            }
+        }
         for (int item = gw; item < T; item += nw) {
             int part, row;
-            if (a.mask) {
+            if (a.mask && !dense) {
                 const int id = kth_active(s_words, s_scan, words, item);
                 part = id < a.rows[0] ? 0 : 1;
                 row = part == 0 ? id : id - a.rows[0];
                 if (lane == 0 && b0 == 0) a.out_idx[part][part == 0 ? item : item - H] = row;
             } else {
-                item_row(a, item, H, part, row);
+                item_row(a, item, H, dense, part, row);
             }
             if ((unsigned)row >= (unsigned)a.rows[part]) {     // id outside the partition: h = 0
                 if (lane == 0)
@@ -541,12 +578,12 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
     const bool active_col = col0 < a.d;
     const int colL = active_col ? col0 : 0;   // lanes past d read column 0, drop the result
     int H, C;
-    item_counts(a, H, C);
+    const bool dense = item_counts(a, H, C);
     int part, lo, hi, nh;
     chunk_range(o.nch, H, C, k, part, lo, hi, nh);
     const int hbase = part == 0 ? 0 : H;
     const uint8_t* base = part == 0 ? a.down[0] : a.down[1];
-    const int32_t* idx = part == 0 ? a.idx[0] : a.idx[1];
+    const int32_t* idx = dense ? nullptr : part == 0 ? a.idx[0] : a.idx[1];
     const int prow_max = part == 0 ? a.rows[0] : a.rows[1];
     const int B = a.B;
     for (int b0 = 0; b0 < B; b0 += BT) {

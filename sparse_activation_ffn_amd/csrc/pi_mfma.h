@@ -37,10 +37,27 @@ constexpr int KS = 128;         // K per pipeline step: one 256-byte LDS row
 constexpr int DC = 128;         // output columns per down workgroup (32 per wave)
 constexpr int DK = 128;         // active rows (K) per down step
 constexpr int MFMA_WG = 256;    // threads of the up and predictor kernels (4 waves)
+constexpr int NXCD = 8;         // accelerator complex dies (XCDs) of the MI355X, one L2 each
 constexpr int DOWN_WG = 256;    // threads of the down kernel (4 waves)
 
 // Byte offset of 16-byte block kb (0..15) of row r in a [rows][256 B] tile.
 __device__ __forceinline__ int swz(int r, int kb) { return r * 256 + 16 * (kb ^ (r & 15)); }
+
+// Weight loads of the up kernel.  A step reads only part of each 128-byte line of
+// a row (Q4_0: 64 bytes of codes); the rest of the line is read one step later,
+// so the loads are ordinary (cached) ones: with non-temporal loads the line was
+// often gone by then (measured FETCH_SIZE, OPT-175B-shaped Q4_0 layer, batch 64:
+// 287 MB non-temporal against 206 MB plain for 199 MB of algorithmic bytes).
+#ifndef PI_UP_NT
+#define PI_UP_NT 0
+#endif
+__device__ __forceinline__ u4 ld16_up(const void* p) {
+#if PI_UP_NT
+    return ld16_stream(p);
+#else
+    return ld16(p);
+#endif
+}
 
 __device__ __forceinline__ f4m mfma32(h8 a, h8 b, f4m c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -161,14 +178,17 @@ __device__ __forceinline__ void up_task(int t, int& r, int& ch) {
 }
 
 // Items [i0, i0 + UR) of an up workgroup -> s_row / s_part (row -1: not a row).
-// With a mask the workgroup scans all of it in LDS (s_words) and emits its own
-// items; workgroup 0 writes the counts and every workgroup its items of the
-// ascending lists.  Returns false (uniformly) when the workgroup has no items.
+// With a mask the workgroup scans all of it in LDS (s_words) and writes the list
+// entries of ranks [i0, i0 + UR); workgroup 0 writes the counts.  When the
+// active count reaches the dense crossover (a.dense_from), the items are all
+// rows of both partitions instead (the lists still name the predicted set).
+// Returns false (uniformly) when the workgroup has no items.
 template <int UR>
 __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, uint64_t* s_words,
                            int& H, int& C) {
     __shared__ int s_cnt[2];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    bool dense;
     if (a.mask) {
         // block-wide scan of the mask words: thread t owns words [t per, t per + per)
         const int words = (a.n + 63) / 64;
@@ -209,7 +229,9 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
             a.out_counts[0] = H;
             a.out_counts[1] = C;
         }
-        // emit the set bits with ranks in [i0, i0 + UR)
+        dense = crosses_to_dense(a, T);
+        // the set bits of ranks [i0, i0 + UR): this workgroup's list entries and,
+        // unless the step crosses to dense, its items
         const int ge = min(T, i0 + UR);
         int r0 = run0;
         for (int w = w0; w < min(words, w0 + per); ++w) {
@@ -223,29 +245,36 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
                     v &= v - 1ull;
                     const int part = rank < H ? 0 : 1;
                     const int row = part == 0 ? id : id - nhot;
-                    const bool ok = (unsigned)row < (unsigned)a.rows[part];
-                    s_row[rank - i0] = ok ? row : -1;
-                    s_part[rank - i0] = part;
+                    if (!dense) {
+                        s_row[rank - i0] = (unsigned)row < (unsigned)a.rows[part] ? row : -1;
+                        s_part[rank - i0] = part;
+                    }
                     a.out_idx[part][part == 0 ? rank : rank - H] = row;
                 }
             }
             r0 += pc;
         }
+        if (dense) {
+            H = a.rows[0];
+            C = a.nparts > 1 ? a.rows[1] : 0;
+        }
         __syncthreads();
     } else {
-        item_counts(a, H, C);
-        if (i0 >= H + C) return false;                    // whole workgroup, uniformly
+        dense = item_counts(a, H, C);
+    }
+    if (i0 >= H + C) return false;                        // whole workgroup, uniformly
+    if (!a.mask || dense) {
         if (tid < UR) {
             const int item = min(i0 + tid, H + C - 1);
             int part, row;
-            item_row(a, item, H, part, row);
+            item_row(a, item, H, dense, part, row);
             if ((unsigned)row >= (unsigned)a.rows[part]) row = -1;
             s_row[tid] = i0 + tid < H + C ? row : -1;
             s_part[tid] = part;
         }
         __syncthreads();
     }
-    return i0 < H + C;
+    return true;
 }
 
 // Bias, activation and the f16 h write of an up tile: lane holds
@@ -338,11 +367,11 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
             for (int g = 0; g < NM; ++g) {
                 if (WT == Q4) {
                     const int blk = k0 / 32 + ch;
-                    R.w[g][j] = ld16_stream(src[g][j] + 16 * (int64_t)blk);
+                    R.w[g][j] = ld16_up(src[g][j] + 16 * (int64_t)blk);
                     R.sc[g][j] = __builtin_bit_cast(
                         _Float16, *reinterpret_cast<const uint16_t*>(src[g][j] + a.d / 2 + 2 * (int64_t)blk));
                 } else {
-                    R.w[g][j] = ld16_stream(src[g][j] + 2 * (int64_t)(k0 + 8 * ch));
+                    R.w[g][j] = ld16_up(src[g][j] + 2 * (int64_t)(k0 + 8 * ch));
                 }
             }
         }
@@ -454,9 +483,17 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
     __shared__ __attribute__((aligned(16))) int s_ids[D + 1][DK];        // row ids of upcoming steps
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
-    const int c0 = blockIdx.x * DC, k = blockIdx.y;
+    // XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin by their
+    // linear id, so workgroup L runs on XCD L % 8.  Chunk k = (L % 8) + 8 m puts
+    // every column tile of one chunk on the same XCD: the chunk's weight rows (each
+    // read by all column tiles, 64-byte pieces of shared 128-byte lines, and the
+    // shared scale lines of Q4_0 rows) and its h slice then come from that XCD's
+    // L2 after the first touch instead of once per XCD from memory.
+    const int tiles = a.d / DC;
+    const int L = blockIdx.x, j = L / NXCD;
+    const int c0 = (j % tiles) * DC, k = L % NXCD + NXCD * (j / tiles);
     int H, C;
-    item_counts(a, H, C);
+    const bool dense = item_counts(a, H, C);
     int part, lo, hi;
     chunk_range8(o.nch, H, C, k, part, lo, hi);
     const int hb = part == 0 ? 0 : round8(H);         // h buffer offset of this partition
@@ -478,7 +515,7 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
         auto row_id = [&](int s) -> int {
             const int item = lo + s * DK + tid;
             const int ic = min(item, hi - 1);
-            const int v = LISTS ? idx[ic] : ic;
+            const int v = (LISTS && !dense) ? idx[ic] : ic;
             return (tid < DK && item < hi && (unsigned)v < (unsigned)prows) ? v : -1;
         };
         struct Stage {

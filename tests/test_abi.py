@@ -155,3 +155,26 @@ def test_noalloc_rejects_shapes_beyond_the_scratch_on_the_host(L):
     assert b"static scratch" in L.pi_last_error()
     assert L.pi_sparse_ffn_split_noalloc(C.byref(hot), None, FAKE, 64, pb.PI_F32, None, None,
                                          None, None, FAKE, None) == pb.PI_ERR_ARG
+
+
+def test_plan_hot_split_matches_the_oracle_rule():
+    """pi_plan_hot_split is host code: its split equals the oracle's rule on the same
+    counts, rates and budgets (integer result, compared exactly)."""
+    import numpy as np
+    from oracle import oracle as O
+    rng = np.random.default_rng(11)
+    for n in (0, 1, 7, 500, 4096):
+        c = np.sort(rng.zipf(1.2, n).clip(max=100_000).astype(np.uint32))[::-1]
+        for h, l in ((5400.0, 54.0), (5400.0, 5400.0), (1.0, 3.0), (8000.0, 0.5)):
+            for budget in (0, 13 * 100, 10 ** 12):
+                got = pb.pi_plan_hot_split(c, budget, 13, h, l)
+                assert got == O.plan_hot_split(c, budget, 13, h, l), (n, h, l, budget)
+    n_hot = C.c_int32(0)
+    assert L_plan_rc(0.0) == pb.PI_ERR_ARG
+    assert pb.lib().pi_plan_hot_split(None, 5, 10, 1, 1.0, 1.0, C.byref(n_hot)) == pb.PI_ERR_ARG
+
+
+def L_plan_rc(rate):
+    n_hot = C.c_int32(0)
+    c = (C.c_uint32 * 3)(3, 2, 1)
+    return pb.lib().pi_plan_hot_split(c, 3, 10, 1, rate, 1.0, C.byref(n_hot))

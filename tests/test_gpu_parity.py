@@ -525,3 +525,108 @@ def test_opt175b_q4_full(B):
     tokens = None if B == 1 else sorted({0, B // 3, (2 * B) // 3, B - 1})
     e, namb, na = check_step(L, wl.n, x, out, tokens=tokens)
     log(f"  q4_0 B={B}: union active {na}, ambiguous {namb}, err {e:.2e}")
+
+
+def test_bandwidth_aware_split_with_cold_rows_in_host_memory():
+    """The hot/cold split chosen from the measured read rates of HBM and of pinned host
+    memory (pi_plan_hot_split) equals the oracle's rule on the same counts and rates; the
+    layer then runs with its cold rows in host memory, checked against the oracle."""
+    wl = SMALL["opt30b-fp16"]
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    X = torch.from_numpy(S.make_profile_x(wl, 0, 256)).to(DEV)
+    counts = dl.profile_counts(X)
+    perm, _ = dl.build_index(counts, S.budget_bytes(wl), S.bytes_per_neuron(wl))
+    torch.cuda.synchronize()
+    perm_np = _np(perm)
+    counts_slot = _np(counts).astype(np.uint32)[perm_np]
+    sink = torch.zeros(pb.PI_STREAM_SINK_WORDS, dtype=torch.int32, device=DEV)
+    rates = []
+    for host in (False, True):
+        nb = 64 << 20
+        buf = torch.empty(nb, dtype=torch.uint8, pin_memory=True) if host else \
+            torch.empty(nb, dtype=torch.uint8, device=DEV)
+        pb.pi_stream_read(buf, nb, sink)
+        torch.cuda.synchronize()
+        pb.pi_kernel_timer_start(pb.PI_K_STREAM, 2)
+        pb.pi_stream_read(buf, nb, sink)
+        pb.pi_stream_read(buf, nb, sink)
+        ms, k = pb.pi_kernel_timer_stop(pb.PI_K_STREAM)
+        rates.append(nb / (ms / k * 1e-3) / 1e9)
+    bpn = S.bytes_per_neuron(wl)
+    budget = wl.n * bpn
+    n_hot = pb.pi_plan_hot_split(counts_slot, budget, bpn, rates[0], rates[1])
+    assert n_hot == O.plan_hot_split(counts_slot, budget, bpn, rates[0], rates[1])
+    log(f"  rates hbm {rates[0]:.0f} GB/s, host {rates[1]:.0f} GB/s -> n_hot {n_hot} of {wl.n}")
+    dl.apply_index(perm, n_hot)
+    dl.place_cold_on_host()
+    Lh = permute_layer(L, perm_np)
+    buf = StepBuffers(dl, 1, DEV)
+    for step in range(3):
+        x = S.make_x(wl, 0, 40 + step, 1)
+        e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x, fused=(step != 1)))
+        log(f"  split from rates, step {step}: active {na}, err {e:.2e}")
+
+
+def _crossover_step(dl, buf, x_np, dense_from, fused_mask=True):
+    x = torch.from_numpy(x_np).to(DEV)
+    hot, cold = dl.parts()
+    buf.hot_idx.fill_(-7)
+    buf.cold_idx.fill_(-7)
+    pb.pi_predict(dl.predictor(), x, buf.mask, None, None if fused_mask else buf.lists, buf.ws)
+    yc = buf.y_cold if cold is not None else None
+    pb.pi_sparse_ffn_crossover(hot, cold, x, buf.lists, dense_from, buf.y_hot, yc, buf.y, buf.ws,
+                               mask=buf.mask if fused_mask else None)
+    torch.cuda.synchronize()
+    c = _np(buf.counts)
+    return dict(mask=_np(buf.mask).view(np.uint64).copy(), counts=c.copy(),
+                hot=_np(buf.hot_idx)[:c[0]].copy(), cold=_np(buf.cold_idx)[:c[1]].copy(),
+                y=_np(buf.y).copy(), y_hot=_np(buf.y_hot).copy(),
+                y_cold=_np(buf.y_cold).copy() if cold is not None else None)
+
+
+@pytest.mark.parametrize("name,B,n_hot", [("reglu-f16", 4, 500), ("q4_0", 20, None),
+                                          ("relu-f16-split", 64, 600), ("q4_0", 2, 400)])
+def test_prompt_phase_crossover(name, B, n_hot):
+    """pi_sparse_ffn_crossover: below the crossover it is the sparse split (bit for bit);
+    from the crossover on, every row of both partitions is computed: the dense FFN of
+    the oracle, with the lists and counts still naming the predicted set."""
+    wl = MFMA_SMALL[name]
+    L = S.make_layer(wl)
+    n_hot = wl.n if n_hot is None else n_hot
+    dl = DeviceLayer.upload(L, DEV, n_hot=n_hot)
+    buf = StepBuffers(dl, B, DEV)
+    x = S.make_x(wl, 0, 1, B)
+    ref = run_step(dl, buf, x, logits=False)
+    T = int(ref["counts"].sum())
+    for fused_mask in (True, False):
+        sparse = _crossover_step(dl, buf, x, T + 1, fused_mask)
+        for k in ("counts", "hot", "cold", "y", "y_hot", "y_cold"):
+            if ref.get(k) is not None:
+                assert np.array_equal(sparse[k], ref[k]), f"sparse side: {k}"
+        dense = _crossover_step(dl, buf, x, T, fused_mask)
+        for k in ("counts", "hot", "cold"):
+            assert np.array_equal(dense[k], ref[k]), f"dense side lists: {k}"
+        yd = O.dense_ffn(O.Part.from_layer(L), x)
+        check_close(dense["y"], yd, wl.wdtype)
+        if n_hot < wl.n:
+            yh = O.dense_ffn(O.Part.from_layer(L, 0, n_hot), x)
+            check_close(dense["y_hot"], yh, wl.wdtype, scale=yd)
+    log(f"  crossover {name} B={B}: {T} active of {wl.n}; dense from {T} matches the dense oracle")
+
+
+@pytest.mark.parametrize("wname,B", [("llama70b-reglu-fp16", 4), ("opt175b-q4_0", 64)])
+def test_dense_path_full_size(wname, B):
+    """The dense side of the crossover at full size (LLaMA(ReGLU)-70B-shaped layer at
+    batch 4, OPT-175B-shaped Q4_0 layer at batch 64) against the oracle's dense FFN on
+    sampled tokens."""
+    wl = S.WORKLOADS[wname]
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    buf = StepBuffers(dl, B, DEV)
+    x = S.make_x(wl, 0, 3, B)
+    out = _crossover_step(dl, buf, x, 1)
+    tokens = sorted({0, B - 1} | ({B // 2} if B > 2 else set()))
+    yd = O.dense_ffn(O.Part.from_layer(L), x[tokens])
+    e = check_close(out["y"][tokens], yd, wl.wdtype)
+    log(f"  dense {wname} B={B}: tokens {tokens} err {e:.2e}")

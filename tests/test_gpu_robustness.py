@@ -176,3 +176,28 @@ def test_threaded_oracle_matches_gpu_step():
     finally:
         O.set_threads(1)
     check_close(out["y"], y, "f16")
+
+
+def test_crossover_on_gathered_path():
+    """The crossover on the gathered two-kernel path (f32 weights, batch 6): dense from
+    the device count on, the oracle's dense FFN; below it, the sparse split."""
+    wl = S.WORKLOADS["opt-fp32"].scaled(d=320, n=1000, r=32)
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV, n_hot=300)
+    buf = StepBuffers(dl, 6, DEV)
+    x_np = S.make_x(wl, 0, 4, 6)
+    ref = _step(dl, buf, x_np)
+    T = int(ref["counts"].sum())
+    x = torch.from_numpy(x_np).to(DEV)
+    hot, cold = dl.parts()
+    for dense_from, want in ((T + 1, "sparse"), (T, "dense")):
+        pb.pi_predict(dl.predictor(), x, buf.mask, None, None, buf.ws)
+        pb.pi_sparse_ffn_crossover(hot, cold, x, buf.lists, dense_from, buf.y_hot, buf.y_cold,
+                                   buf.y, buf.ws, mask=buf.mask)
+        torch.cuda.synchronize()
+        y = _np(buf.y)
+        assert np.array_equal(_np(buf.counts), ref["counts"])
+        if want == "sparse":
+            assert np.array_equal(y, ref["y"])
+        else:
+            check_close(y, O.dense_ffn(O.Part.from_layer(L), x_np), "f32")
