@@ -199,6 +199,68 @@ def per_step_us(torch, step, idxs):
     return np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev[:-1], ev[1:])])
 
 
+def adaptive_predictor(pb, torch, S, wl, layer, buf, xs, idxs, dev, target=0.99):
+    """Recall-calibrated threshold on the workload's profiling samples (computed on the
+    GPU by pi_calibrate_threshold), then, on held-out decode inputs, the predicted set
+    against the true firing set (pi_true_mask) at that threshold and at the default one.
+    layer: the whole layer in device memory (predictor and rows in the same order)."""
+    X = torch.from_numpy(S.make_profile_x(wl, 0)).to(dev)
+    nS = X.shape[0]
+    ws = torch.empty(pb.pi_calibrate_workspace_bytes(wl.d, wl.n, wl.r, nS), dtype=torch.uint8,
+                     device=dev)
+    tau = torch.empty(1, dtype=torch.float32, device=dev)
+    stats = torch.empty(3, dtype=torch.int32, device=dev)
+    part = layer.part()
+    pb.pi_calibrate_threshold(layer.predictor(), part, X, target, tau, stats, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    pb.pi_calibrate_threshold(layer.predictor(), part, X, target, tau, stats, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    cal_ms = e0.elapsed_time(e1)
+    t = float(tau.item())
+    N, m, hits = (int(v) for v in stats.cpu().numpy())
+    del ws, X
+    n = wl.n
+    tm = torch.empty((n + 63) // 64, dtype=torch.int64, device=dev)
+
+    def bits(words):
+        return np.unpackbits(words.cpu().numpy().view(np.uint8), bitorder="little")[:n].astype(bool)
+
+    preds = {"default_threshold": layer.predictor(),
+             "adaptive": pb.make_predictor(layer.P1t, layer.P2t, layer.b2, t)}
+    hot, cold = layer.parts()
+    rows = {}
+    for name, pred in preds.items():
+        tp = npred = ntrue = 0
+        for i in idxs:
+            pb.pi_predict(pred, xs[i], buf.mask, None, None, buf.ws)
+            pb.pi_true_mask(part, xs[i], tm)
+            pm, tt = bits(buf.mask), bits(tm)
+            tp += int((pm & tt).sum())
+            npred += int(pm.sum())
+            ntrue += int(tt.sum())
+
+        def step(i, pred=pred):
+            pb.pi_predict(pred, xs[i], buf.mask, None, None, buf.ws)
+            pb.pi_sparse_ffn_split(hot, cold, xs[i], buf.lists, None, None, buf.y, buf.ws,
+                                   mask=buf.mask)
+        per = per_step_us(torch, step, idxs)
+        rows[name] = {"threshold": preds[name].threshold,
+                      "recall": round(tp / max(ntrue, 1), 5),
+                      "precision": round(tp / max(npred, 1), 5),
+                      "density": round(npred / (len(idxs) * n), 5),
+                      "us_per_step_p50": round(float(np.median(per)), 3)}
+    return {"target_recall": target, "samples": nS, "tau": t, "firing_pairs": N, "m": m,
+            "calibration_recall": round(hits / max(N, 1), 6),
+            "calibration_ms": round(cal_ms, 3), "decode_steps": len(idxs),
+            "true_density": round(ntrue / (len(idxs) * n), 5), **rows,
+            "note": "held-out decode inputs; the random-init predictor is independent of the "
+                    "layer's firing beyond the per-neuron rates, so the density needed for a "
+                    "recall target is far above a trained predictor's"}
+
+
 def draw_stack(wl, dev):
     """The Falcon-40B-shaped stack: 60 distinct layers drawn on the GPU
     (workload.synth.make_layer_device), each profiled on 1024 samples, indexed under its
@@ -502,6 +564,11 @@ def main():
             "touched_bytes_per_step": round(step_bytes(wl, B, la)),
             "achieved_gbps_touched": round(step_bytes(wl, B, la) / (lit_us * 1e-6) / 1e9, 1),
             "note": "predictor without its output bias (b2 = 0, threshold 0), eager launches"}
+
+        if wl.hot_frac is not None and not args.cold_host:
+            log("[bench] adaptive predictor threshold ...")
+            extras["adaptive_predictor"] = adaptive_predictor(pb, torch, S, wl, base, buf, xs,
+                                                              list(range(W, W + K)), dev)
 
     dense = None
     if not args.no_dense:

@@ -278,6 +278,42 @@ pi_status pi_build_neuron_index(const uint32_t* counts, int32_t n, int64_t budge
                                 void* stream);
 
 /*
+ * Adaptive predictor threshold (chatpaper.ai abstract: adaptive predictors;
+ * hada.io README summary, hybrid-approach section: a predictor adapted per
+ * layer), chosen offline on profiling samples to reach a recall target.
+ * Over the S samples of X [S][d] (xdtype PI_F32 or PI_F16) the call computes
+ * on the GPU, in float32 as the decode path does:
+ *   logit(s, i)  = the predictor's logit (the kernels of pi_predict, in
+ *                  batches of up to PI_MAX_BATCH samples),
+ *   firing(s, i) = the deciding pre-activation of neuron i (W_up + b_up, or
+ *                  W_gate + b_gate for ReGLU) is > 0,
+ * and, with N firing pairs and m = ceil(target_recall * N), returns in *tau
+ * (device float) the largest float32 threshold for which at least m firing
+ * pairs have logit > tau: the float32 just below the m-th largest logit among
+ * the firing pairs (an exact radix selection with integer histograms; FLT_MAX
+ * when N == 0).  stats (device uint32 [3]): N, m, and the firing pairs whose
+ * logit is > tau (>= m).  Using tau as pi_predictor.threshold gives recall >=
+ * target_recall on these samples.  part must be the whole layer (rows == n, same
+ * d) in the predictor's neuron order.  target_recall in (0, 1]; S * n <= 2^31.
+ * Needs a workspace of pi_calibrate_workspace_bytes(d, n, r, S) bytes.
+ */
+size_t pi_calibrate_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t S);
+pi_status pi_calibrate_threshold(const pi_predictor* p, const pi_ffn_part* part, const void* X,
+                                 int32_t S, int32_t xdtype, double target_recall, float* tau,
+                                 uint32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The true firing set of a batch, for measuring a predictor's recall and
+ * precision: bit i % 64 of mask word i / 64 is set iff the deciding
+ * pre-activation of neuron i (as in pi_calibrate_threshold) is > 0 for some
+ * token of x [B][d] (float32 decision).  mask [ceil(part->rows / 64)] uint64
+ * device, 8-byte aligned, overwritten (tail bits 0).  Reads every row of the
+ * deciding matrix (a dense pass; measurement only).
+ */
+pi_status pi_true_mask(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                       uint64_t* mask, void* stream);
+
+/*
  * Hot/cold split from the tiers' read rates and the capacity budget (CSDN
  * article, overall-architecture section: neurons are placed from their
  * activation frequencies and the hardware's bandwidth and capacity;

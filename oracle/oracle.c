@@ -48,6 +48,7 @@
  * are also reported in float32 rounding of the fp64 value, the precision the
  * GPU library decides in, for the comparison protocol of the tests.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -462,6 +463,94 @@ int or_plan_hot_split(const uint32_t* counts_slot, int64_t n, int64_t budget_byt
     int64_t k = best_k < cap ? best_k : cap;
     *n_hot = k < n ? k : n;
     return OR_OK;
+}
+
+/*
+ * Adaptive predictor threshold (chatpaper.ai abstract: adaptive predictors;
+ * hada.io README summary, hybrid-approach section: an adaptive predictor per
+ * layer).  Over the S profiling samples of X[S][d]:
+ *   firing(s, i) = the deciding pre-activation of neuron i (as in
+ *                  or_profile_counts) is > 0,
+ *   logit(s, i)  = the predictor's logit (as in or_predict).
+ * Both are decided in float32 rounding of the double values, the precision the
+ * GPU library computes them in.  With N firing pairs and m = ceil(target * N),
+ * the threshold is the largest float32 tau for which at least m firing pairs
+ * have logit > tau, i.e. the float32 just below the m-th largest logit among
+ * the firing pairs; the recall #{firing, logit > tau} / N is then >= target.
+ * N == 0 gives tau = FLT_MAX (nothing fires, nothing need be predicted).
+ * Outputs: *tau, stats[0] = N, stats[1] = m, stats[2] = firing pairs with
+ * logit > tau.
+ */
+static int or_cmp_float_desc(const void* a, const void* b)
+{
+    float fa = *(const float*)a, fb = *(const float*)b;
+    return (fa < fb) - (fa > fb);
+}
+
+int or_calibrate_threshold(int64_t d, int64_t n, int64_t r, int pdtype, const void* P1t,
+                           const void* P2t, const float* b2, const or_part* part, const void* X,
+                           int xdtype, int64_t S, double target, float* tau, int64_t* stats)
+{
+    if (d <= 0 || n <= 0 || S < 0 || part->rows != n || part->d != d || !(target > 0.0) ||
+        target > 1.0)
+        return OR_BAD;
+    const void* W = part->act == OR_REGLU ? part->W_gate : part->W_up;
+    const float* bias = part->act == OR_REGLU ? part->b_gate : part->b_up;
+    double* logits = malloc(sizeof(double) * (n > 0 ? n : 1));
+    double* xs = malloc(sizeof(double) * d);
+    signed char* fire = malloc((size_t)n);
+    float* fired = malloc(sizeof(float) * (S * n > 0 ? S * n : 1));
+    uint64_t* mask = malloc(sizeof(uint64_t) * ((n + 63) / 64));
+    if (!logits || !xs || !fire || !fired || !mask) {
+        free(logits); free(xs); free(fire); free(fired); free(mask);
+        return OR_BAD;
+    }
+    int64_t N = 0;
+    int rc = OR_OK;
+    for (int64_t s = 0; s < S && rc == OR_OK; ++s) {
+        /* the predictor's logits for sample s */
+        const uint8_t* xb = (const uint8_t*)X + s * d * (xdtype == OR_F32 ? 4 : 2);
+        rc = or_predict(d, n, r, pdtype, P1t, P2t, b2, 0.0, xb, xdtype, 1, mask, logits, NULL);
+        or_load_x(X, xdtype, d, s, xs);
+        /* firing decided per neuron (independent), collected in neuron order */
+#pragma omp parallel num_threads(or_nthreads) if (or_nthreads > 1)
+        {
+            double* rw = malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < n; ++i) {
+                if (!rw) { fire[i] = -1; continue; }
+                or_load_row(W, part->wdtype, d, i, rw);
+                double pre = or_dot(rw, xs, d) + (bias ? (double)bias[i] : 0.0);
+                fire[i] = (float)pre > 0.0f;
+            }
+            free(rw);
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            if (fire[i] < 0) rc = OR_BAD;
+            else if (fire[i]) fired[N++] = (float)logits[i];
+        }
+    }
+    if (rc == OR_OK) {
+        int64_t m = (int64_t)ceil(target * (double)N);
+        if (m < 1 && N > 0) m = 1;
+        if (m > N) m = N;
+        float t;
+        int64_t hits = 0;
+        if (N == 0) {
+            t = FLT_MAX;
+        } else {
+            qsort(fired, (size_t)N, sizeof(float), or_cmp_float_desc);
+            t = nextafterf(fired[m - 1], -INFINITY);
+        }
+        for (int64_t k = 0; k < N; ++k)
+            hits += fired[k] > t;
+        *tau = t;
+        stats[0] = N;
+        stats[1] = m;
+        stats[2] = hits;
+    }
+    free(logits); free(xs); free(fire); free(fired); free(mask);
+    return rc;
 }
 
 /* ---- one whole layer step ---------------------------------------------- */

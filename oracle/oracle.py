@@ -64,6 +64,7 @@ def lib():
         _lib.or_profile_counts.argtypes = [P, P, I, I64, P, P, P, D]
         _lib.or_build_neuron_index.argtypes = [P, I64, I64, I64, P, P]
         _lib.or_plan_hot_split.argtypes = [P, I64, I64, I64, D, D, P]
+        _lib.or_calibrate_threshold.argtypes = [I64, I64, I64, I, P, P, P, P, P, I, I64, D, P, P]
         _lib.or_layer_step.argtypes = [I64, I64, I64, I, P, P, P, D, P, P, P, I, I64, P, P, P, P,
                                        P]
     return _lib
@@ -239,6 +240,23 @@ def plan_hot_split(counts_slot, budget_bytes, bytes_per_neuron, hbm_rate, link_r
     if rc:
         raise ValueError("or_plan_hot_split rejected its arguments")
     return int(out.value)
+
+
+def calibrate_threshold(P1t, P2t, b2, part: Part, X, target):
+    """Adaptive threshold: the largest float32 tau with recall >= target over the firing
+    (sample, neuron) pairs of X.  Returns (tau, N firing pairs, m, firing pairs above tau)."""
+    P1t, P2t, X = (np.ascontiguousarray(a) for a in (P1t, P2t, X))
+    r, d = P1t.shape
+    n = P2t.shape[0]
+    b2 = None if b2 is None else np.ascontiguousarray(b2, dtype=np.float32)
+    tau = np.zeros(1, np.float32)
+    stats = np.zeros(3, np.int64)
+    rc = lib().or_calibrate_threshold(d, n, r, _dtype_code(P1t), _ptr(P1t), _ptr(P2t), _ptr(b2),
+                                      C.byref(part.s), _ptr(X), _dtype_code(X), X.shape[0],
+                                      float(target), _ptr(tau), _ptr(stats))
+    if rc:
+        raise ValueError("or_calibrate_threshold rejected its arguments")
+    return float(tau[0]), int(stats[0]), int(stats[1]), int(stats[2])
 
 
 def layer_step(P1t, P2t, b2, threshold, hot: Part, cold, x):

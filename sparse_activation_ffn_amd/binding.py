@@ -31,6 +31,7 @@ EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_
            "pi_sparse_ffn_crossover", "pi_merge",
            "pi_dense_ffn",
            "pi_profile_counts", "pi_build_neuron_index", "pi_plan_hot_split",
+           "pi_calibrate_workspace_bytes", "pi_calibrate_threshold", "pi_true_mask",
            "pi_accumulate_mask", "pi_permute_rows",
            "pi_copy", "pi_stream_read",
            "pi_kernel_timer_start", "pi_kernel_timer_stop", "pi_kernel_name", "pi_status_string",
@@ -87,6 +88,9 @@ def lib() -> C.CDLL:
         "pi_profile_counts": ([P, P, I32, I32, P, P], I32),
         "pi_build_neuron_index": ([P, I32, I64, I64, P, P, P], I32),
         "pi_plan_hot_split": ([P, I32, I64, I64, C.c_double, C.c_double, P], I32),
+        "pi_calibrate_workspace_bytes": ([I32, I32, I32, I32], SZ),
+        "pi_calibrate_threshold": ([P, P, P, I32, I32, C.c_double, P, P, P, SZ, P], I32),
+        "pi_true_mask": ([P, P, I32, I32, P, P], I32),
         "pi_accumulate_mask": ([P, I32, P, P], I32),
         "pi_permute_rows": ([P, P, P, I32, I64, P], I32),
         "pi_copy": ([P, P, I64, P], I32),
@@ -233,6 +237,23 @@ def pi_plan_hot_split(counts_slot, budget_bytes: int, bytes_per_neuron: int, hbm
                                    int(bytes_per_neuron), float(hbm_gbps), float(link_gbps),
                                    C.byref(n_hot)))
     return int(n_hot.value)
+
+
+def pi_calibrate_workspace_bytes(d: int, n: int, r: int, S: int) -> int:
+    return int(lib().pi_calibrate_workspace_bytes(d, n, r, S))
+
+
+def pi_calibrate_threshold(pred: Predictor, part: FfnPart, X, target_recall: float, tau, stats,
+                           ws, stream=None):
+    _check(lib().pi_calibrate_threshold(C.byref(pred), C.byref(part), ptr(X), X.shape[0],
+                                        dtype_code(X), float(target_recall), ptr(tau), ptr(stats),
+                                        ptr(ws), ws.numel() * ws.element_size(),
+                                        stream_handle(stream)))
+
+
+def pi_true_mask(part: FfnPart, x, mask, stream=None):
+    _check(lib().pi_true_mask(C.byref(part), ptr(x), x.shape[0], dtype_code(x), ptr(mask),
+                              stream_handle(stream)))
 
 
 def pi_accumulate_mask(mask, n: int, counts, stream=None):

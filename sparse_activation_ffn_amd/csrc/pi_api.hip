@@ -543,6 +543,39 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     return run_ffn(a, o, wt, xdtype, hot->act, n, s);
 }
 
+// The predictor's kernels for B tokens (validated arguments; `base` is a
+// workspace of at least ws_pred_bytes(r, B) bytes).
+pi_status predict_launch(const pi_predictor* p, const void* x, int B, int xdtype, uint64_t* mask,
+                         float* logits, uint8_t* base, hipStream_t s) {
+    float* u = reinterpret_cast<float*>(base + WS_CTR_BYTES);
+    const int wt = p->wdtype;
+    if (B >= MFMA_MIN_BATCH && wt == F16 && xdtype == F16 && p->r % KS == 0 && p->d % KS == 0) {
+        // matrix-core predictor: K-split first layer, slice sum + ReLU, second layer
+        float* uscale = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * p->r * 4));
+        float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(uscale) + align256((size_t)B * 4));
+        const dim3 g1((p->r + P1_ROWS - 1) / P1_ROWS, P1_KS);
+        const int mt = mfma_mt(B);
+        auto pred1 = mt == 1 ? k_mfma_pred1<1> : mt == 2 ? k_mfma_pred1<2> : k_mfma_pred1<4>;
+        TRY(launch(PI_K_PRED_L1, pred1, g1, dim3(MFMA_WG), 0, s, (const uint8_t*)p->P1t,
+                   (const uint8_t*)x, p->d, p->r, B, part));
+        TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(B), dim3(THREADS), 0, s, (const float*)part, B, p->r,
+                   u, uscale));
+        auto pred2 = mt == 1 ? k_mfma_pred2<1> : mt == 2 ? k_mfma_pred2<2> : k_mfma_pred2<4>;
+        TRY(launch(PI_K_PRED_L2, pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
+                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, (const float*)uscale,
+                   p->n, p->r, B, mask, logits));
+    } else {
+        pi_status st;
+        if (wt == F32)
+            st = xdtype == F32 ? pred_l1_bt<F32, F32>(p, x, B, u, s) : pred_l1_bt<F32, F16>(p, x, B, u, s);
+        else
+            st = xdtype == F32 ? pred_l1_bt<F16, F32>(p, x, B, u, s) : pred_l1_bt<F16, F16>(p, x, B, u, s);
+        TRY(st);
+        TRY(wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, s) : pred_l2_bt<F16>(p, u, B, mask, logits, s));
+    }
+    return PI_OK;
+}
+
 }  // namespace
 
 // =================================================================================
@@ -624,36 +657,23 @@ pi_status pi_predict(const pi_predictor* p, const void* x, int32_t B, int32_t xd
         L = Lists{lists->n_hot, lists->hot_idx, lists->cold_idx, lists->counts};
     }
     TRY(check_ws(ws, ws_bytes, ws_pred_bytes(p->r, B)));
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    float* u = reinterpret_cast<float*>(base + WS_CTR_BYTES);
     hipStream_t s = (hipStream_t)stream;
-    const int wt = p->wdtype;
-    if (B >= MFMA_MIN_BATCH && wt == F16 && xdtype == F16 && p->r % KS == 0 && p->d % KS == 0) {
-        // matrix-core predictor: K-split first layer, slice sum + ReLU, second layer
-        float* uscale = reinterpret_cast<float*>(base + WS_CTR_BYTES + align256((size_t)B * p->r * 4));
-        float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(uscale) + align256((size_t)B * 4));
-        const dim3 g1((p->r + P1_ROWS - 1) / P1_ROWS, P1_KS);
-        const int mt = mfma_mt(B);
-        auto pred1 = mt == 1 ? k_mfma_pred1<1> : mt == 2 ? k_mfma_pred1<2> : k_mfma_pred1<4>;
-        TRY(launch(PI_K_PRED_L1, pred1, g1, dim3(MFMA_WG), 0, s, (const uint8_t*)p->P1t,
-                   (const uint8_t*)x, p->d, p->r, B, part));
-        TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(B), dim3(THREADS), 0, s, (const float*)part, B, p->r,
-                   u, uscale));
-        auto pred2 = mt == 1 ? k_mfma_pred2<1> : mt == 2 ? k_mfma_pred2<2> : k_mfma_pred2<4>;
-        TRY(launch(PI_K_PRED_L2, pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
-                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, (const float*)uscale,
-                   p->n, p->r, B, mask, logits));
-    } else {
-        pi_status st;
-        if (wt == F32)
-            st = xdtype == F32 ? pred_l1_bt<F32, F32>(p, x, B, u, s) : pred_l1_bt<F32, F16>(p, x, B, u, s);
-        else
-            st = xdtype == F32 ? pred_l1_bt<F16, F32>(p, x, B, u, s) : pred_l1_bt<F16, F16>(p, x, B, u, s);
-        TRY(st);
-        TRY(wt == F32 ? pred_l2_bt<F32>(p, u, B, mask, logits, s) : pred_l2_bt<F16>(p, u, B, mask, logits, s));
-    }
+    TRY(predict_launch(p, x, B, xdtype, mask, logits, static_cast<uint8_t*>(ws), s));
     if (!lists) return PI_OK;
     return launch(PI_K_COMPACT, k_compact, dim3(1), dim3(THREADS), 0, s, (const uint64_t*)mask, p->n, L);
+}
+
+// ---- adaptive predictor threshold (offline) -----------------------------------
+// workspace: logits [S][n] f32, keys [n][S] u32, the selection histogram and
+// state, a mask word per 64 neurons, then the predictor's own scratch
+static size_t calib_layout(int32_t d, int32_t n, int32_t r, int32_t S, size_t off[5]) {
+    off[0] = WS_CTR_BYTES;                                          // logits
+    off[1] = off[0] + align256((size_t)S * n * 4);                  // keys
+    off[2] = off[1] + align256((size_t)S * n * 4);                  // hist [SEL_BINS] + state [8]
+    off[3] = off[2] + align256((SEL_BINS + 8) * 4);                 // mask words
+    off[4] = off[3] + align256((size_t)(n + 63) / 64 * 8);          // predictor scratch
+    (void)d;
+    return off[4] + ws_pred_bytes(r, PI_MAX_BATCH);
 }
 
 pi_status pi_compact_active(const uint64_t* mask, int32_t n, const pi_active_lists* lists,
@@ -796,6 +816,93 @@ pi_status pi_plan_hot_split(const uint32_t* counts_slot, int32_t n, int64_t budg
     const int64_t cap = budget_bytes / bytes_per_neuron;
     *n_hot = (int32_t)std::min<int64_t>(std::min<int64_t>(best, cap), n);
     return PI_OK;
+}
+
+size_t pi_calibrate_workspace_bytes(int32_t d, int32_t n, int32_t r, int32_t S) {
+    if (d <= 0 || n <= 0 || r <= 0 || S <= 0 || (int64_t)S * n > (int64_t)1 << 31) return 0;
+    size_t off[5];
+    return calib_layout(d, n, r, S, off);
+}
+
+pi_status pi_calibrate_threshold(const pi_predictor* p, const pi_ffn_part* part, const void* X,
+                                 int32_t S, int32_t xdtype, double target_recall, float* tau,
+                                 uint32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+    CHECK(p && part, PI_ERR_ARG, "predictor and partition required");
+    CHECK(p->wdtype == PI_F32 || p->wdtype == PI_F16, PI_ERR_DTYPE, "predictor wdtype must be PI_F32 or PI_F16");
+    TRY(check_dtype_x(xdtype));
+    TRY(check_part(part, "part", false));
+    CHECK(p->d > 0 && p->d % 64 == 0 && p->r > 0 && p->r % 16 == 0 && p->r <= 4096, PI_ERR_SHAPE,
+          "predictor d or r out of range");
+    CHECK(part->rows == p->n && part->d == p->d, PI_ERR_SHAPE,
+          "the partition must be the whole layer (rows == n, same d) in the predictor's neuron order");
+    CHECK(S >= 1 && (int64_t)S * p->n <= (int64_t)1 << 31, PI_ERR_SHAPE, "S * n must be in 1..2^31");
+    CHECK(target_recall > 0.0 && target_recall <= 1.0, PI_ERR_ARG, "target_recall must be in (0, 1]");
+    CHECK(p->P1t && p->P2t && X && tau && stats, PI_ERR_ARG, "P1t, P2t, X, tau and stats required");
+    CHECK(aligned(p->P1t, 16) && aligned(p->P2t, 16) && aligned(X, 16) && aligned(tau, 4) && aligned(stats, 4) &&
+          aligned(p->b2, 4), PI_ERR_ALIGN, "misaligned pointer");
+    size_t off[5];
+    TRY(check_ws(ws, ws_bytes, calib_layout(p->d, p->n, p->r, S, off)));
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    float* logits = reinterpret_cast<float*>(base + off[0]);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(base + off[1]);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(base + off[2]);
+    uint32_t* state = hist + SEL_BINS;
+    uint64_t* mask = reinterpret_cast<uint64_t*>(base + off[3]);
+    hipStream_t s = (hipStream_t)stream;
+    // 1. the predictor's logits for every sample, in batches the library computes at decode
+    const int64_t xrow = (int64_t)p->d * (xdtype == PI_F32 ? 4 : 2);
+    for (int s0 = 0; s0 < S; s0 += PI_MAX_BATCH) {
+        const int nb = std::min(PI_MAX_BATCH, S - s0);
+        TRY(predict_launch(p, static_cast<const uint8_t*>(X) + s0 * xrow, nb, xdtype, mask,
+                           logits + (int64_t)s0 * p->n, base + off[4], s));
+    }
+    // 2. keys of the firing pairs
+    const bool reglu = part->act == PI_REGLU;
+    const uint8_t* W = (const uint8_t*)(reglu ? part->W_gate : part->W_up);
+    const float* bias = reglu ? part->b_gate : part->b_up;
+    const int grid = (part->rows + NWAVES - 1) / NWAVES;
+    const int wt = part->wdtype;
+#define FIRE(WT_, XT_) launch(PI_K_PROFILE, k_fire_keys<WT_, XT_, 8>, dim3(grid), dim3(THREADS), 0, s, \
+                              W, bias, (const uint8_t*)X, part->d, part->rows, S, (const float*)logits, keys)
+    if (wt == F32) TRY(xdtype == F32 ? FIRE(F32, F32) : FIRE(F32, F16));
+    else if (wt == F16) TRY(xdtype == F32 ? FIRE(F16, F32) : FIRE(F16, F16));
+    else TRY(xdtype == F32 ? FIRE(Q4, F32) : FIRE(Q4, F16));
+#undef FIRE
+    // 3. exact selection of the m-th largest key: digits of 11, 11 and 10 bits
+    const int64_t len = (int64_t)S * p->n;
+    const int64_t n16 = (SEL_BINS + 8) * 4 / 16;
+    TRY(launch(PI_K_INDEX, k_zero, dim3(1), dim3(THREADS), 0, s, reinterpret_cast<u4*>(hist), n16));
+    int hgrid = (int)std::min<int64_t>(1024, (len + THREADS - 1) / THREADS);
+    const int shifts[3] = {21, 10, 0}, bits[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+        TRY(launch(PI_K_INDEX, k_key_hist, dim3(hgrid), dim3(THREADS), 0, s, (const uint32_t*)keys, len,
+                   (const uint32_t*)state, shifts[pass], bits[pass], hist));
+        TRY(launch(PI_K_INDEX, k_key_select, dim3(1), dim3(THREADS), 0, s, hist, shifts[pass], bits[pass],
+                   pass == 0 ? 1 : 0, target_recall, state));
+    }
+    TRY(launch(PI_K_INDEX, k_key_finish, dim3(1), dim3(64), 0, s, (const uint32_t*)state, tau, stats));
+    return launch(PI_K_INDEX, k_key_count, dim3(hgrid), dim3(THREADS), 0, s, (const uint32_t*)keys, len,
+                  (const float*)tau, stats);
+}
+
+pi_status pi_true_mask(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                       uint64_t* mask, void* stream) {
+    TRY(check_part(part, "part", false));
+    TRY(check_dtype_x(xdtype));
+    CHECK(B >= 1 && B <= PI_MAX_BATCH, PI_ERR_SHAPE, "B must be in 1..%d", PI_MAX_BATCH);
+    CHECK(x && mask && aligned(x, 16) && aligned(mask, 8), PI_ERR_ARG, "x (16-byte) and mask (8-byte) required");
+    const bool reglu = part->act == PI_REGLU;
+    const uint8_t* W = (const uint8_t*)(reglu ? part->W_gate : part->W_up);
+    const float* bias = reglu ? part->b_gate : part->b_up;
+    const int grid = (part->rows + 63) / 64;
+    hipStream_t s = (hipStream_t)stream;
+    const int wt = part->wdtype;
+#define TM(WT_, XT_) launch(PI_K_PROFILE, k_true_mask<WT_, XT_>, dim3(grid), dim3(THREADS), 0, s, \
+                            W, bias, (const uint8_t*)x, part->d, part->rows, B, mask)
+    if (wt == F32) return xdtype == F32 ? TM(F32, F32) : TM(F32, F16);
+    if (wt == F16) return xdtype == F32 ? TM(F16, F32) : TM(F16, F16);
+    return xdtype == F32 ? TM(Q4, F32) : TM(Q4, F16);
+#undef TM
 }
 
 pi_status pi_accumulate_mask(const uint64_t* mask, int32_t n, uint32_t* counts, void* stream) {

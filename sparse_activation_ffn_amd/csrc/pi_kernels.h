@@ -742,6 +742,191 @@ __global__ __launch_bounds__(THREADS) void k_profile(const uint8_t* __restrict__
 }
 
 // ===========================================================================
+// Adaptive predictor threshold (offline): the firing (sample, neuron) pairs'
+// logits as order-preserving integer keys, then an exact radix selection of
+// the m-th largest (three passes of 11, 11 and 10 bits, integer histograms).
+// ===========================================================================
+// key(a) < key(b) iff a < b for non-NaN floats (-0 just below +0); 0 is never a
+// key of a float (the smallest, key(-inf), is 0x007fffff) and marks "no pair".
+__device__ __forceinline__ uint32_t fkey(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+    return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// keys[i * S + s] = fkey(logits[s * rows + i]) if neuron i fires on sample s
+// (deciding pre-activation > 0, decided in float32 as k_profile decides), else 0.
+// One wave per neuron, samples in groups of BT.
+template <int WT, int XT, int BT>
+__global__ __launch_bounds__(THREADS) void k_fire_keys(const uint8_t* __restrict__ W,
+                                                       const float* __restrict__ bias,
+                                                       const uint8_t* __restrict__ X, int d, int rows,
+                                                       int S, const float* __restrict__ logits,
+                                                       uint32_t* __restrict__ keys) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int XB = XT == F32 ? 4 : 2;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int row = (blockIdx.x * THREADS + threadIdx.x) / WAVE;
+    if (row >= rows) return;
+    const int64_t rb = row_bytes(WT, d);
+    const uint8_t* w = W + (int64_t)row * rb;
+    const int nch = d / EPC;
+    const float bi = bias ? bias[row] : 0.0f;
+    for (int s0 = 0; s0 < S; s0 += BT) {
+        float acc[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) acc[b] = 0.0f;
+        for (int c = lane; c < nch; c += WAVE) {
+            const u4 v = ld16(w + 16 * (int64_t)c);
+            const float sc = WT == Q4 ? half_f(*(const uint16_t*)(w + d / 2 + 2 * c)) : 0.0f;
+#pragma unroll
+            for (int b = 0; b < BT; ++b)
+                if (s0 + b < S)
+                    acc[b] = Dot<WT, XT>::run(v, sc, X + ((int64_t)(s0 + b) * d + c * EPC) * XB, acc[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            const float pre = wave_sum(acc[b]) + bi;
+            if (lane == b && s0 + b < S)
+                keys[(int64_t)row * S + s0 + b] = pre > 0.0f ? fkey(logits[(int64_t)(s0 + b) * rows + row]) : 0u;
+        }
+    }
+}
+
+// Selection state: [0] key prefix fixed so far, [1] its bit mask, [2] rank still
+// wanted below the prefix (1 = the largest), [3] N keys, [4] m = ceil(target N).
+constexpr int SEL_BINS = 2048;
+
+// hist[digit] += number of keys that carry the current prefix, by their `bits`-bit
+// digit at `shift` (bits <= 11)
+__global__ __launch_bounds__(THREADS) void k_key_hist(const uint32_t* __restrict__ keys, int64_t len,
+                                                      const uint32_t* __restrict__ state, int shift,
+                                                      int bits, uint32_t* __restrict__ hist) {
+    __shared__ uint32_t s_h[SEL_BINS];
+    for (int b = threadIdx.x; b < SEL_BINS; b += THREADS) s_h[b] = 0u;
+    __syncthreads();
+    const uint32_t prefix = state[0], pmask = state[1], dmask = (1u << bits) - 1u;
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t j = (int64_t)blockIdx.x * THREADS + threadIdx.x; j < len; j += stride) {
+        const uint32_t k = keys[j];
+        if (k != 0u && (k & pmask) == prefix) atomicAdd(&s_h[(k >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < SEL_BINS; b += THREADS)
+        if (s_h[b]) atomicAdd(&hist[b], s_h[b]);
+}
+
+// One workgroup: fixes the next digit of the m-th largest key and clears hist.
+__global__ __launch_bounds__(THREADS) void k_key_select(uint32_t* __restrict__ hist, int shift, int bits,
+                                                        int first, double target, uint32_t* __restrict__ state) {
+    if (threadIdx.x == 0) {
+        const int bins = 1 << bits;
+        if (first) {
+            uint32_t N = 0;
+            for (int b = 0; b < bins; ++b) N += hist[b];
+            uint32_t m = (uint32_t)ceil(target * (double)N);
+            if (N > 0 && m < 1) m = 1;
+            if (m > N) m = N;
+            state[2] = m;
+            state[3] = N;
+            state[4] = m;
+        }
+        const uint32_t rem = state[2];
+        if (rem > 0) {
+            uint32_t cum = 0;
+            for (int b = bins - 1; b >= 0; --b) {
+                const uint32_t h = hist[b];
+                if (cum + h >= rem) {
+                    state[0] |= (uint32_t)b << shift;
+                    state[1] |= (uint32_t)(bins - 1) << shift;
+                    state[2] = rem - cum;
+                    break;
+                }
+                cum += h;
+            }
+        }
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < SEL_BINS; b += THREADS) hist[b] = 0u;
+}
+
+// tau = the float just below the selected logit (FLT_MAX without keys);
+// stats [0] = N, [1] = m, [2] = 0 (counted by k_key_count)
+__global__ void k_key_finish(const uint32_t* __restrict__ state, float* __restrict__ tau,
+                             uint32_t* __restrict__ stats) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const uint32_t N = state[3];
+        *tau = N ? nextafterf(fkey_inv(state[0]), -INFINITY) : 3.402823466e38f;
+        stats[0] = N;
+        stats[1] = state[4];
+        stats[2] = 0u;
+    }
+}
+
+// stats[2] += number of keys whose logit is > tau
+__global__ __launch_bounds__(THREADS) void k_key_count(const uint32_t* __restrict__ keys, int64_t len,
+                                                       const float* __restrict__ tau,
+                                                       uint32_t* __restrict__ stats) {
+    __shared__ uint32_t s_c[NWAVES];
+    const uint32_t kt = fkey(*tau);
+    uint32_t c = 0;
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t j = (int64_t)blockIdx.x * THREADS + threadIdx.x; j < len; j += stride) {
+        const uint32_t k = keys[j];
+        c += (k != 0u && k > kt) ? 1u : 0u;
+    }
+    c = (uint32_t)wave_sum_int((int)c);
+    if ((threadIdx.x & (WAVE - 1)) == 0) s_c[threadIdx.x / WAVE] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < NWAVES; ++w) t += s_c[w];
+        if (t) atomicAdd(&stats[2], t);
+    }
+}
+
+// The true firing set of a batch: bit i of mask = OR over tokens of (deciding
+// pre-activation of neuron i > 0, in float32).  One workgroup per mask word:
+// each wave decides 16 neurons, then one ballot writes the word.
+template <int WT, int XT>
+__global__ __launch_bounds__(THREADS) void k_true_mask(const uint8_t* __restrict__ W,
+                                                       const float* __restrict__ bias,
+                                                       const uint8_t* __restrict__ X, int d, int rows,
+                                                       int B, uint64_t* __restrict__ mask) {
+    constexpr int EPC = Chunk<WT>::EPC;
+    constexpr int XB = XT == F32 ? 4 : 2;
+    __shared__ unsigned s_fire[64];
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int64_t rb = row_bytes(WT, d);
+    const int nch = d / EPC;
+    for (int j = 0; j < 16; ++j) {
+        const int loc = 16 * wv + j, row = 64 * blockIdx.x + loc;
+        unsigned fire = 0;
+        if (row < rows) {
+            const uint8_t* w = W + (int64_t)row * rb;
+            const float bi = bias ? bias[row] : 0.0f;
+            for (int b = 0; b < B; ++b) {
+                float acc = 0.0f;
+                for (int c = lane; c < nch; c += WAVE) {
+                    const u4 v = ld16(w + 16 * (int64_t)c);
+                    const float sc = WT == Q4 ? half_f(*(const uint16_t*)(w + d / 2 + 2 * c)) : 0.0f;
+                    acc = Dot<WT, XT>::run(v, sc, X + ((int64_t)b * d + c * EPC) * XB, acc);
+                }
+                fire |= (wave_sum(acc) + bi) > 0.0f ? 1u : 0u;
+            }
+        }
+        if (lane == 0) s_fire[loc] = fire;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const uint64_t word = __ballot(s_fire[lane] != 0u);
+        if (lane == 0) mask[blockIdx.x] = word;
+    }
+}
+
+// ===========================================================================
 // Neuron index: rank_i = #{j : c_j > c_i} + #{j < i : c_j == c_i}; perm[rank_i] = i.
 // Exact, deterministic, O(n^2) compares over LDS tiles of the counts.
 // ===========================================================================

@@ -178,3 +178,25 @@ def L_plan_rc(rate):
     n_hot = C.c_int32(0)
     c = (C.c_uint32 * 3)(3, 2, 1)
     return pb.lib().pi_plan_hot_split(c, 3, 10, 1, rate, 1.0, C.byref(n_hot))
+
+
+def test_calibrate_and_true_mask_validation(L):
+    pred = _pred(d=256, n=100)
+    part = _part()
+    wsb = L.pi_calibrate_workspace_bytes(256, 100, 16, 200)
+    assert wsb > 200 * 100 * 8
+    assert L.pi_calibrate_workspace_bytes(256, 100, 16, 0) == 0
+
+    def cal(p=pred, q=part, S=200, target=0.99, ws=FAKE, n=wsb):
+        return L.pi_calibrate_threshold(C.byref(p), C.byref(q), FAKE, S, pb.PI_F16, target,
+                                        FAKE, FAKE, ws, n, None)
+    assert cal(target=0.0) == pb.PI_ERR_ARG
+    assert cal(target=1.5) == pb.PI_ERR_ARG
+    assert cal(q=_part(rows=99)) == pb.PI_ERR_SHAPE           # not the whole layer
+    assert cal(q=_part(d=512)) == pb.PI_ERR_SHAPE
+    assert cal(S=0) == pb.PI_ERR_SHAPE
+    assert cal(p=_pred(d=256, n=100, wdtype=pb.PI_Q4_0)) == pb.PI_ERR_DTYPE
+    assert cal(n=wsb - 16) == pb.PI_ERR_WORKSPACE
+    assert L.pi_true_mask(C.byref(part), FAKE, 0, pb.PI_F16, FAKE, None) == pb.PI_ERR_SHAPE
+    assert L.pi_true_mask(C.byref(part), FAKE, 1, pb.PI_F16, FAKE + 4, None) == pb.PI_ERR_ARG
+    assert L.pi_true_mask(C.byref(_part(d=100)), FAKE, 1, pb.PI_F16, FAKE, None) == pb.PI_ERR_SHAPE
