@@ -261,6 +261,54 @@ def adaptive_predictor(pb, torch, S, wl, layer, buf, xs, idxs, dev, target=0.99)
                     "recall target is far above a trained predictor's"}
 
 
+def prompt_crossover(pb, torch, S, StepBuffers, wl, layer, dev, batches=(8, 16, 32, 64), steps=8):
+    """The prompt-phase crossover on the indexed layer: per batch, the sparse split and
+    the dense FFN taken through pi_sparse_ffn_crossover (dense_from = n + 1 and 1), the
+    predictor alone, and the crossover count that the measured times give (the active
+    count at which the sparse FFN's per-row cost reaches the dense FFN's time); then
+    the same steps with that count, the device choosing per step."""
+    hot, cold = layer.parts()
+    pred = layer.predictor()
+    rows = []
+    for B in batches:
+        buf = StepBuffers(layer, B, dev)
+        xs = [torch.from_numpy(S.make_x(wl, 0, 100000 + s, B)).to(dev) for s in range(steps)]
+
+        def predict(i):
+            pb.pi_predict(pred, xs[i], buf.mask, None, None, buf.ws)
+
+        def step(i, dense_from):
+            predict(i)
+            pb.pi_sparse_ffn_crossover(hot, cold, xs[i], buf.lists, dense_from, None, None, buf.y,
+                                       buf.ws, mask=buf.mask)
+
+        def timed(fn):
+            fn(0)
+            torch.cuda.synchronize()
+            return float(np.median(per_step_us(torch, fn, list(range(steps)))))
+        active = []
+        for i in range(steps):
+            step(i, wl.n + 1)
+            active.append(int(buf.counts.sum().item()))
+        t_pred = timed(predict)
+        t_sparse = timed(lambda i: step(i, wl.n + 1))
+        t_dense = timed(lambda i: step(i, 1))
+        a = float(np.mean(active))
+        per_row = max(t_sparse - t_pred, 1e-3) / max(a, 1.0)
+        dense_from = max(1, min(wl.n + 1, int(np.ceil((t_dense - t_pred) / per_row))))
+        t_chosen = timed(lambda i: step(i, dense_from))
+        rows.append({"batch": B, "mean_active": round(a, 1), "density": round(a / wl.n, 4),
+                     "predict_us": round(t_pred, 2), "sparse_us": round(t_sparse, 2),
+                     "dense_us": round(t_dense, 2), "dense_from": dense_from,
+                     "dense_steps": int(sum(c >= dense_from for c in active)),
+                     "chosen_us": round(t_chosen, 2)})
+        del buf, xs
+    return {"workload": wl.name, "steps_per_batch": steps, "rows": rows,
+            "note": "median step time from HIP events between eagerly launched steps; dense_from "
+                    "= the active count where predict + per-row sparse cost reaches the dense "
+                    "step, applied on the device per step"}
+
+
 def draw_stack(wl, dev):
     """The Falcon-40B-shaped stack: 60 distinct layers drawn on the GPU
     (workload.synth.make_layer_device), each profiled on 1024 samples, indexed under its
@@ -565,6 +613,9 @@ def main():
             "achieved_gbps_touched": round(step_bytes(wl, B, la) / (lit_us * 1e-6) / 1e9, 1),
             "note": "predictor without its output bias (b2 = 0, threshold 0), eager launches"}
 
+        if B == 1 and not args.cold_host and wl.xdtype == "f16":
+            log("[bench] prompt-phase crossover over batches ...")
+            extras["prompt_crossover"] = prompt_crossover(pb, torch, S, StepBuffers, wl, base, dev)
         if wl.hot_frac is not None and not args.cold_host:
             log("[bench] adaptive predictor threshold ...")
             extras["adaptive_predictor"] = adaptive_predictor(pb, torch, S, wl, base, buf, xs,
