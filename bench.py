@@ -87,18 +87,23 @@ def step_bytes(wl, B, active):
     return pred + active * (m * wrow_bytes(wl) + 4) + B * wl.d * esize(wl.xdtype) + 4 * B * wl.d
 
 
-def counter_traffic(wl_name, kernel):
+KERNEL_SOURCES = ("pi_device.h", "pi_kernels.h", "pi_ffn.h", "pi_mfma.h", "pi_api.hip")
+
+
+def counter_traffic(wl_name, kernel, B=1):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter record
-    (profiles/<workload>_traffic.json: FETCH_SIZE and WRITE_SIZE passes scaled by a
-    plain copy of known size), or None when there is no record or the kernel sources
-    changed since the counters were taken."""
+    (profiles/<workload>_traffic.json at batch 1, <workload>_b<B>_traffic.json
+    otherwise: FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy of known
+    size), or None when there is no record or the kernel sources changed since the
+    counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{wl_name}_traffic.json")
+    name = f"{wl_name}_traffic.json" if B == 1 else f"{wl_name}_b{B}_traffic.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
-    for f in ("pi_device.h", "pi_kernels.h", "pi_ffn.h", "pi_api.hip"):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "sparse_activation_ffn_amd", "csrc", f), "rb").read())
     k = rec.get("kernels", {}).get(kernel)
     if rec.get("source_sha256") != h.hexdigest() or k is None:
@@ -568,7 +573,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbps, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
                 "algorithmic_bytes": round(kb_mean[dom]),
-                "traffic": counter_traffic(wl.name, dom), "target_frac": TARGET_FRAC}
+                "traffic": counter_traffic(wl.name, dom, B), "target_frac": TARGET_FRAC}
 
     extras = {}
     if not args.no_extras:
