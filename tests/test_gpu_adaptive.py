@@ -144,6 +144,31 @@ def test_selection_is_exact_on_device_values(name):
     assert hits == int((f > want).sum())
 
 
+def test_calibration_full_size_layer():
+    """OPT-30B-shaped layer (d 7168, n 28672, r 1024), 96 profiling samples (one batch of
+    64 and a ragged one of 32), target 0.99: tau against the oracle's order statistics."""
+    wl = S.WORKLOADS["opt30b-fp16"]
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    X_np = S.make_profile_x(wl, 0, 96)
+    X = torch.from_numpy(X_np).to(DEV)
+    tau, (N, m, hits) = _calibrate(dl, X, 0.99)
+    O.set_threads(oracle_threads())
+    try:
+        tau_o, N_o, m_o, _ = O.calibrate_threshold(L.P1t, L.P2t, L.b2, O.Part.from_layer(L), X_np, 0.99)
+        logits, pre = _oracle_pairs(L, X_np)
+    finally:
+        O.set_threads(1)
+    fire_o = pre.astype(np.float32) > 0
+    k_amb = int((np.abs(pre) <= FIRE_BAND).sum())
+    log(f"  device tau {tau!r} N {N} m {m} hits {hits}; oracle tau {tau_o!r} N {N_o} m {m_o}; "
+        f"{k_amb} ambiguous pairs")
+    assert abs(N - N_o) <= k_amb and hits >= m
+    f = np.sort(logits[fire_o].astype(np.float32))[::-1]
+    v = float(np.nextafter(np.float32(tau), np.float32(np.inf)))
+    assert f[min(m - 1 + k_amb, N_o - 1)] - LOGIT_TOL <= v <= f[max(m - 1 - k_amb, 0)] + LOGIT_TOL
+
+
 def test_no_firing_pair_gives_flt_max():
     wl = S.WORKLOADS["opt-fp32"].scaled(d=320, n=1000, r=32)
     L = S.make_layer(wl)

@@ -155,6 +155,20 @@ def test_small_parity(name, B):
         log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
 
 
+def test_gathered_path_with_more_than_64k_of_lds():
+    """f32 weights at batch 6 take the gathered two-kernel path; at d = 2048 the
+    token group of x (8 x 2048 fp32 = 64 KiB) plus the mask words and their scan
+    exceed 64 KiB of dynamic LDS, which the kernel must be granted explicitly."""
+    wl = S.WORKLOADS["opt-fp32"].scaled(d=2048, n=3000, r=64)
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    buf = StepBuffers(dl, 6, DEV)
+    for step in range(2):
+        x = S.make_x(wl, 0, step, 6)
+        e, namb, na = check_step(L, wl.n, x, run_step(dl, buf, x, fused=(step == 0)))
+        log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
+
+
 SQRELU_SMALL = {
     "f16": S.WORKLOADS["opt30b-fp16"].scaled(d=576, n=2085, r=64, act="sqrelu"),
     "f32": S.WORKLOADS["opt-fp32"].scaled(d=320, n=1000, r=32, act="sqrelu"),
