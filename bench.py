@@ -103,7 +103,7 @@ def counter_traffic(wl_name, kernel, B=1):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in rec.get("sources", KERNEL_SOURCES):   # the files the measured kernels come from
         h.update(open(os.path.join(ROOT, "sparse_activation_ffn_amd", "csrc", f), "rb").read())
     k = rec.get("kernels", {}).get(kernel)
     if rec.get("source_sha256") != h.hexdigest() or k is None:

@@ -413,25 +413,35 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
         for (int jn = 0; jn < NT; ++jn)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[g][jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
+    // every fragment of the step is read before the first product: the LDS
+    // latency is paid once per step, not once per 32-wide K slice
     auto compute = [&]() {
+        constexpr int NKS = KS / 32;
+        h8 ax[NKS][MT], bw[NKS][NM][NT];
 #pragma unroll
-        for (int ks = 0; ks < KS / 32; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             const int kb = 4 * ks + q;
-            h8 ax[MT], bw[NM][NT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) ax[mt] = *reinterpret_cast<const h8*>(s_x + swz(16 * mt + c, kb));
-#pragma unroll
-            for (int g = 0; g < NM; ++g)
-#pragma unroll
-                for (int jn = 0; jn < NT; ++jn)
-                    bw[g][jn] = *reinterpret_cast<const h8*>(s_w[g] + swz(16 * NT * wv + 16 * jn + c, kb));
+            for (int mt = 0; mt < MT; ++mt) ax[ks][mt] = *reinterpret_cast<const h8*>(s_x + swz(16 * mt + c, kb));
 #pragma unroll
             for (int g = 0; g < NM; ++g)
 #pragma unroll
                 for (int jn = 0; jn < NT; ++jn)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[g][jn][mt] = mfma32(ax[mt], bw[g][jn], acc[g][jn][mt]);
+                    bw[ks][g][jn] = *reinterpret_cast<const h8*>(s_w[g] + swz(16 * NT * wv + 16 * jn + c, kb));
         }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int g = 0; g < NM; ++g)
+#pragma unroll
+                for (int jn = 0; jn < NT; ++jn)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[g][jn][mt] = mfma32(ax[ks][mt], bw[ks][g][jn], acc[g][jn][mt]);
+        // keep the order: the compiler's scheduler would interleave each product
+        // with its own fragment reads again
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS * (MT + NM * NT), 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, NKS * NM * NT * MT, 0);     // matrix-core ops
     };
     run_pipeline<D, Stage>(0, a.d / KS, load, store, compute);
     up_epilogue<ACT, NM, NT, MT>(a, acc, s_row, s_part, i0, H, T, h16);
