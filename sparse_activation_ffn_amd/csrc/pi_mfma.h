@@ -118,32 +118,57 @@ __device__ __forceinline__ int h_pos(int item, int H) { return item < H ? item :
 
 // Software pipeline over K steps [s0, s1): D stages of global loads in a
 // register ring; step s's registers go to LDS, then step s + D is loaded into
-// the freed registers while the matrix cores work on step s.  The loop body is
-// the same on every path: every stage issues the same loads (past the end it
-// reloads the last step), and the padding steps of the last round are stored
-// with their token operand zeroed (store(R, false)) and computed, adding exact
-// zeros.  The compiler's wait counts are then static inside a round, so a store
-// waits only for its own stage, never for the D - 1 stages issued after it.
-template <int D, typename Stage, int ROUND = 12 / D * D, typename Load, typename Store, typename Compute>
+// the freed registers while the matrix cores work on step s.  Every stage
+// issues the same loads (past the end it reloads the last step), so the
+// compiler's wait counts are static inside an unrolled round and a store waits
+// only for its own stage, never for the D - 1 stages issued after it.  The
+// compiler cannot carry exact wait counts around a loop back edge (it waits for
+// everything at the loop head), so the steps run in rounds of ROUND steps
+// (several rings); the remainder runs in rings of D steps whose padding steps
+// past the end are stored with their token operand zeroed (store(R, false))
+// and computed, adding exact zeros.
+template <int D, int ROUND, typename Stage, typename Step>
+__device__ __forceinline__ void pipeline_rounds(int s0, int s1, Stage (&R)[D], Step step) {
+    static_assert(ROUND % D == 0, "a round is whole rings");
+    int sb = s0;
+    for (; sb + ROUND <= s1; sb += ROUND) {
+#pragma unroll
+        for (int dd = 0; dd < ROUND; ++dd) step(R[dd % D], sb + dd, true);
+    }
+    for (; sb < s1; sb += D) {
+#pragma unroll
+        for (int dd = 0; dd < D; ++dd) step(R[dd % D], sb + dd, sb + dd < s1);
+    }
+}
+
+// Rounds of ROUND steps only, the last one padded (one copy of the body: for
+// step counts that are a multiple of ROUND, where the remainder loop's extra
+// code only costs registers).
+template <int D, int ROUND, typename Stage, typename Step>
+__device__ __forceinline__ void pipeline_rounds_padded(int s0, int s1, Stage (&R)[D], Step step) {
+    static_assert(ROUND % D == 0, "a round is whole rings");
+    for (int sb = s0; sb < s1; sb += ROUND) {
+#pragma unroll
+        for (int dd = 0; dd < ROUND; ++dd) step(R[dd % D], sb + dd, sb + dd < s1);
+    }
+}
+
+template <int D, typename Stage, int ROUND = 12 / D * D, bool PADDED = false, typename Load, typename Store,
+          typename Compute>
 __device__ __forceinline__ void run_pipeline(int s0, int s1, Load load, Store store, Compute compute) {
     if (s1 <= s0) return;                             // uniform
     Stage R[D];
 #pragma unroll
     for (int dd = 0; dd < D; ++dd) load(R[dd], min(s0 + dd, s1 - 1));
-    // the compiler cannot carry exact wait counts around a loop back edge (it
-    // waits for everything at the loop head), so a round is several rings long
-    static_assert(ROUND % D == 0, "a round is whole rings");
-    for (int sb = s0; sb < s1; sb += ROUND) {
-#pragma unroll
-        for (int dd = 0; dd < ROUND; ++dd) {
-            const int s = sb + dd;
-            __syncthreads();                          // the previous step's LDS reads are done
-            store(R[dd % D], s < s1);
-            load(R[dd % D], min(s + D, s1 - 1));
-            __syncthreads();
-            compute();
-        }
-    }
+    auto step = [&](Stage& St, int s, bool live) {
+        __syncthreads();                              // the previous step's LDS reads are done
+        store(St, live);
+        load(St, min(s + D, s1 - 1));
+        __syncthreads();
+        compute();
+    };
+    if constexpr (PADDED) pipeline_rounds_padded<D, ROUND>(s0, s1, R, step);
+    else pipeline_rounds<D, ROUND>(s0, s1, R, step);
 }
 
 // ===========================================================================
@@ -626,22 +651,18 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
         Stage R[D];
 #pragma unroll
         for (int dd = 0; dd < D; ++dd) load(R[dd], min(dd, steps - 1));
-        constexpr int ROUND = D;                  // one ring per round (see run_pipeline)
-        for (int sb = 0; sb < steps; sb += ROUND) {
-#pragma unroll
-            for (int dd = 0; dd < ROUND; ++dd) {
-                // same body on every path (see run_pipeline): padding steps of
-                // the last round store a zero h tile and add exact zeros
-                const int s = sb + dd;
-                __syncthreads();                      // the previous step's LDS reads are done
-                store(R[dd % D], s < steps);
-                if (tid < DK) s_ids[(s + D) % (D + 1)][tid] = nid;
-                __syncthreads();
-                nid = row_id(s + D + 1);
-                load(R[dd % D], min(s + D, steps - 1));
-                compute();
-            }
-        }
+        // one ring per round (measured: rounds of several rings here were slower,
+        // 121 -> 157 us on the Q4_0 batch-64 layer); padding steps past the end
+        // store a zero h tile and add exact zeros
+        pipeline_rounds_padded<D, D>(0, steps, R, [&](Stage& St, int s, bool live) {
+            __syncthreads();                          // the previous step's LDS reads are done
+            store(St, live);
+            if (tid < DK) s_ids[(s + D) % (D + 1)][tid] = nid;
+            __syncthreads();
+            nid = row_id(s + D + 1);
+            load(St, min(s + D, steps - 1));
+            compute();
+        });
     }
     // partial of y: lane holds D[token 16 mt + 4 q + i][column 32 wv + 16 jn + c]
 #pragma unroll
@@ -901,7 +922,7 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
             }
         }
     };
-    run_pipeline<D, Stage, 8>(0, r / KS, load, store, compute);     // r = 1024: one round
+    run_pipeline<D, Stage, 8, true>(0, r / KS, load, store, compute);     // r = 1024: one round
     // lane holds D[token 16 mt + 4 q + i][neuron 32 wv + 16 jn + c]
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
