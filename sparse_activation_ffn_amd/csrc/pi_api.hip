@@ -103,8 +103,10 @@ bool use_fused(int d, int wt, int xt, int B) {
 // ReGLU 70B layer 130 vs 163 us per layer step; at batch 1 the fused kernel
 // wins, 48 vs 77 us on the OPT-30B layer).
 constexpr int MFMA_MIN_BATCH = 2;
-bool use_mfma(int d, int wt, int xt, int B) {
-    return B >= MFMA_MIN_BATCH && B <= MM && xt == F16 && (wt == F16 || wt == Q4) && d % DC == 0;
+bool use_mfma(int d, int wt, int xt, int B, int64_t max_rows = 0) {
+    // (the Q4_0 down kernel addresses a partition with 32-bit offsets)
+    return B >= MFMA_MIN_BATCH && B <= MM && xt == F16 && (wt == F16 || wt == Q4) && d % DC == 0 &&
+           (wt != Q4 || max_rows * row_bytes(Q4, d) < ((int64_t)1 << 31));
 }
 // split-K chunks of the matrix-core down kernel: about two workgroups per
 // compute unit, a multiple of the 8 XCDs (each XCD takes whole chunks)
@@ -471,7 +473,7 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     }
     const int d = hot->d, wt = hot->wdtype;
     const int n = hot->rows + (has_cold ? cold->rows : 0);
-    const bool mfma = use_mfma(d, wt, xdtype, B);
+    const bool mfma = use_mfma(d, wt, xdtype, B, std::max<int64_t>(hot->rows, has_cold ? cold->rows : 0));
     // the dense crossover is decided on the device by the two-kernel paths; the
     // fused batch-1 kernel does not take it
     const bool fused = !mfma && dense_from <= 0 && use_fused(d, wt, xdtype, B);

@@ -428,7 +428,9 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
 #pragma unroll
         for (int j = 0; j < XJ; ++j) {
             const int t = tid + MFMA_WG * j, m = t >> 4, kb = t & 15;
-            if (t < XN) *reinterpret_cast<u4*>(s_x + swz(m, kb)) = (act && m < a.B) ? R.xv[j] : u4{0u, 0u, 0u, 0u};
+            // (token rows past B hold copies of row B - 1; their output rows are
+            // never stored)
+            if (t < XN) *reinterpret_cast<u4*>(s_x + swz(m, kb)) = act ? R.xv[j] : u4{0u, 0u, 0u, 0u};
         }
     };
     f4m acc[NM][NT][MT];
@@ -539,6 +541,16 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
     // this thread's 8 x 8 weight block: rows 8 rg .. +7 of the step, columns 8 cg .. +7
     const int cg = tid & 15, rg = tid >> 4;
     const int col0 = c0 + 8 * cg;
+    // Q4_0 rows are addressed by 32-bit offsets from the partition base (the host
+    // keeps Q4_0 partitions on this path below 2 GiB): a base in scalar registers
+    // plus a 32-bit offset is one load operand, instead of 64-bit arithmetic
+    // per row
+    const uint64_t bu = reinterpret_cast<uint64_t>(base);
+    typedef const __attribute__((address_space(1))) uint8_t gbyte;
+    gbyte* const wb = (gbyte*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(bu >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bu));
+    const unsigned coff = 16u * (unsigned)(col0 >> 5) + (unsigned)(col0 & 15);      // 8 code bytes
+    const unsigned soff = (unsigned)(a.d / 2) + 2u * (unsigned)(col0 >> 5);          // the block's scale
     f4m acc[2][MT];
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
@@ -560,6 +572,7 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
             u4 hv[HJ];
             unsigned rows_ok;         // bit r: row r is a row (else its weights are zeroed)
             int hvalid[HJ];           // items of each h load that are in the chunk
+            bool full;                // every item of the step is in the chunk
         };
         // loads of step s (its row ids are in s_ids[s % (D + 1)]); all unconditional
         auto load = [&](Stage& R, int s) {
@@ -568,14 +581,15 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int row = ids[8 * rg + r];
-                R.rows_ok |= (row >= 0 ? 1u : 0u) << r;
-                const uint8_t* rowp = base + (int64_t)(row >= 0 ? row : 0) * a.rb;
                 if (WT == Q4) {
-                    const int blk = col0 >> 5, t0 = col0 & 31;
-                    R.cq[r] = *reinterpret_cast<const u2*>(rowp + 16 * (int64_t)blk + (t0 & 15));
-                    R.sc[r] = __builtin_bit_cast(
-                        _Float16, *reinterpret_cast<const uint16_t*>(rowp + a.d / 2 + 2 * (int64_t)blk));
+                    // a non-row reads row 0 and gets a zero scale (zero weights)
+                    R.rows_ok |= (row >= 0 ? 1u : 0u) << r;
+                    const unsigned ro = (unsigned)max(row, 0) * (unsigned)a.rb;
+                    R.cq[r] = *(const __attribute__((address_space(1))) u2*)(wb + (ro + coff));
+                    R.sc[r] = *(const __attribute__((address_space(1))) _Float16*)(wb + (ro + soff));
                 } else {
+                    R.rows_ok |= (row >= 0 ? 1u : 0u) << r;
+                    const uint8_t* rowp = base + (int64_t)(row >= 0 ? row : 0) * a.rb;
                     R.w[r] = ld16_stream(rowp + 2 * (int64_t)col0);
                 }
             }
@@ -585,8 +599,11 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
             for (int j = 0; j < HJ; ++j) {
                 const int t = min(tid + DOWN_WG * j, HN - 1), m = t >> 4, kb = t & 15;
                 R.hv[j] = ld16(h16 + (int64_t)min(m, a.B - 1) * a.h_ld + hb + min(i0 + 8 * kb, last));
-                R.hvalid[j] = m < a.B ? hi - (i0 + 8 * kb) : 0;   // items past hi are zero
+                // items past hi are zeroed (token rows past B hold copies of row B - 1
+                // and give output rows that are never stored)
+                R.hvalid[j] = hi - (i0 + 8 * kb);
             }
+            R.full = i0 + DK <= hi;
         };
         auto store = [&](const Stage& R, bool act) {
             unsigned V[8][4];                           // V[r][p] = columns 2p, 2p+1 of row r
@@ -609,17 +626,25 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
                 out.w = __builtin_amdgcn_perm(V[7][p], V[6][p], sel);
                 *reinterpret_cast<u4*>(s_wt + wt_off(8 * cg + cc, rg)) = out;
             }
+            if (act && R.full) {                        // (uniform) the usual step: no item to mask
 #pragma unroll
-            for (int j = 0; j < HJ; ++j) {
-                const int t = tid + DOWN_WG * j, m = t >> 4, kb = t & 15;
-                const u4 v = R.hv[j];
-                const int valid = act ? R.hvalid[j] : 0;
-                if (t < HN)
-                    *reinterpret_cast<u4*>(s_h + swz(m, kb)) =
-                        u4{valid >= 2 ? v.x : (valid == 1 ? v.x & 0xffffu : 0u),
-                           valid >= 4 ? v.y : (valid == 3 ? v.y & 0xffffu : 0u),
-                           valid >= 6 ? v.z : (valid == 5 ? v.z & 0xffffu : 0u),
-                           valid >= 8 ? v.w : (valid == 7 ? v.w & 0xffffu : 0u)};
+                for (int j = 0; j < HJ; ++j) {
+                    const int t = tid + DOWN_WG * j, m = t >> 4, kb = t & 15;
+                    if (t < HN) *reinterpret_cast<u4*>(s_h + swz(m, kb)) = R.hv[j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < HJ; ++j) {
+                    const int t = tid + DOWN_WG * j, m = t >> 4, kb = t & 15;
+                    const u4 v = R.hv[j];
+                    const int valid = act ? R.hvalid[j] : 0;
+                    if (t < HN)
+                        *reinterpret_cast<u4*>(s_h + swz(m, kb)) =
+                            u4{valid >= 2 ? v.x : (valid == 1 ? v.x & 0xffffu : 0u),
+                               valid >= 4 ? v.y : (valid == 3 ? v.y & 0xffffu : 0u),
+                               valid >= 6 ? v.z : (valid == 5 ? v.z & 0xffffu : 0u),
+                               valid >= 8 ? v.w : (valid == 7 ? v.w & 0xffffu : 0u)};
+                }
             }
         };
         auto compute = [&]() {
