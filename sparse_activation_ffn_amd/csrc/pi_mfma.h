@@ -63,11 +63,17 @@ __device__ __forceinline__ f4m mfma32(h8 a, h8 b, f4m c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Two 4-bit codes (bits 0..3 and 16..19 of v) -> two f16 values (q - 8) * s,
-// each rounded once: 0x6400 | q is the f16 1024 + q, and 1024 + q - 1032 is exact
-// (the "magic number" int4-to-fp16 conversion of Kim et al., arXiv 2211.10017).
-__device__ __forceinline__ unsigned q4_pair(unsigned v, h2v s2) {
-    const unsigned bits = (v & 0x000f000fu) | 0x64006400u;
+// Two 4-bit codes -> two f16 values (q - 8) * s, each rounded once: the f16
+// with bits 0x6400 | q is 1024 + q, and 1024 + q - 1032 is exact (the "magic
+// number" int4-to-fp16 conversion of Kim et al., arXiv 2211.10017).  q4_bits
+// builds the two halves 0x640q from two bytes of v in one byte permute (the
+// 0x64 bytes come from the constant operand) and one AND that keeps the low
+// nibbles; sel picks bytes 0, 1 (Q4_SEL01) or 2, 3 (Q4_SEL23) of v.
+constexpr unsigned Q4_SEL01 = 0x04010400u, Q4_SEL23 = 0x04030402u;
+__device__ __forceinline__ unsigned q4_bits(unsigned v, unsigned sel) {
+    return __builtin_amdgcn_perm(0x64646464u, v, sel) & 0xff0fff0fu;
+}
+__device__ __forceinline__ unsigned q4_scaled(unsigned bits, h2v s2) {
     h2v t = __builtin_bit_cast(h2v, bits);
     t = (t - h2v{(_Float16)1032.0f, (_Float16)1032.0f}) * s2;
     return __builtin_bit_cast(unsigned, t);
@@ -82,12 +88,11 @@ __device__ __forceinline__ void deq_block(u4 c, _Float16 s, u4 out[4]) {
     unsigned lo[8], hi[8];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const unsigned a01 = __builtin_amdgcn_perm(0u, w[p], 0x0c010c00u);   // bytes 0, 1
-        const unsigned a23 = __builtin_amdgcn_perm(0u, w[p], 0x0c030c02u);   // bytes 2, 3
-        lo[2 * p] = q4_pair(a01, s2);
-        lo[2 * p + 1] = q4_pair(a23, s2);
-        hi[2 * p] = q4_pair(a01 >> 4, s2);
-        hi[2 * p + 1] = q4_pair(a23 >> 4, s2);
+        const unsigned ws = w[p] >> 4;                 // high nibbles moved to the low ones
+        lo[2 * p] = q4_scaled(q4_bits(w[p], Q4_SEL01), s2);
+        lo[2 * p + 1] = q4_scaled(q4_bits(w[p], Q4_SEL23), s2);
+        hi[2 * p] = q4_scaled(q4_bits(ws, Q4_SEL01), s2);
+        hi[2 * p + 1] = q4_scaled(q4_bits(ws, Q4_SEL23), s2);
     }
     out[0] = u4{lo[0], lo[1], lo[2], lo[3]};
     out[1] = u4{lo[4], lo[5], lo[6], lo[7]};
@@ -103,8 +108,8 @@ __device__ __forceinline__ u4 deq8(u2 c, _Float16 s, bool high) {
     unsigned o[4];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        o[2 * p] = q4_pair(__builtin_amdgcn_perm(0u, w[p], 0x0c010c00u), s2);
-        o[2 * p + 1] = q4_pair(__builtin_amdgcn_perm(0u, w[p], 0x0c030c02u), s2);
+        o[2 * p] = q4_scaled(q4_bits(w[p], Q4_SEL01), s2);
+        o[2 * p + 1] = q4_scaled(q4_bits(w[p], Q4_SEL23), s2);
     }
     return u4{o[0], o[1], o[2], o[3]};
 }
