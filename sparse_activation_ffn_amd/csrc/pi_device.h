@@ -113,9 +113,9 @@ template <> struct Dot<F16, F32> {
 // This integer-to-half conversion by OR-ing codes into the mantissa of a
 // power-of-two constant is the published "magic number" method for 4-bit
 // weights (Kim et al., arXiv 2211.10017, fast int4-to-fp16 conversion).
-__device__ __forceinline__ h2 q4_pair(unsigned two_bytes_in_halves) {
-    h2 v = bits_h2((two_bytes_in_halves & 0x000F000Fu) | 0x64006400u);
-    return v - h2{(_Float16)1032.0f, (_Float16)1032.0f};
+// q4_pair takes the two halves already as 0x640q.
+__device__ __forceinline__ h2 q4_pair(unsigned halves_0x640q) {
+    return bits_h2(halves_0x640q) - h2{(_Float16)1032.0f, (_Float16)1032.0f};
 }
 
 template <> struct Dot<Q4, F16> {
@@ -129,13 +129,19 @@ template <> struct Dot<Q4, F16> {
         float blk = 0.0f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            // bytes (0,1) and (2,3) of code dword m moved into the two halves
-            unsigned b01 = __builtin_amdgcn_perm(cw[m], cw[m], 0x0C010C00u);
-            unsigned b23 = __builtin_amdgcn_perm(cw[m], cw[m], 0x0C030C02u);
-            blk = __builtin_amdgcn_fdot2(q4_pair(b01), bits_h2(xl[2 * m]), blk, false);
-            blk = __builtin_amdgcn_fdot2(q4_pair(b23), bits_h2(xl[2 * m + 1]), blk, false);
-            blk = __builtin_amdgcn_fdot2(q4_pair(b01 >> 4), bits_h2(xh[2 * m]), blk, false);
-            blk = __builtin_amdgcn_fdot2(q4_pair(b23 >> 4), bits_h2(xh[2 * m + 1]), blk, false);
+            // bytes (0,1) and (2,3) of code dword m into the two halves, each as
+            // 0x64 above its byte (one permute: the 0x64 bytes come from the
+            // constant operand), then the low nibble kept; the high nibbles the
+            // same way from the dword shifted by 4
+            const unsigned ws = cw[m] >> 4;
+            const unsigned l01 = __builtin_amdgcn_perm(0x64646464u, cw[m], 0x04010400u) & 0xff0fff0fu;
+            const unsigned l23 = __builtin_amdgcn_perm(0x64646464u, cw[m], 0x04030402u) & 0xff0fff0fu;
+            const unsigned h01 = __builtin_amdgcn_perm(0x64646464u, ws, 0x04010400u) & 0xff0fff0fu;
+            const unsigned h23 = __builtin_amdgcn_perm(0x64646464u, ws, 0x04030402u) & 0xff0fff0fu;
+            blk = __builtin_amdgcn_fdot2(q4_pair(l01), bits_h2(xl[2 * m]), blk, false);
+            blk = __builtin_amdgcn_fdot2(q4_pair(l23), bits_h2(xl[2 * m + 1]), blk, false);
+            blk = __builtin_amdgcn_fdot2(q4_pair(h01), bits_h2(xh[2 * m]), blk, false);
+            blk = __builtin_amdgcn_fdot2(q4_pair(h23), bits_h2(xh[2 * m + 1]), blk, false);
         }
         return fmaf(blk, s, acc);
     }
