@@ -131,6 +131,88 @@ def host_cpu():
     return model, nproc, max(1, threads)
 
 
+def hybrid_cpu_cold(pb, torch, wl, L, perm_np, layers, buf, xs, idxs, dev, threads):
+    """The pages' hybrid step (CSDN article, CPU/GPU hybrid-design section and figure):
+    the hot partition's rows in HBM computed by the GPU, the cold partition's rows in
+    host memory computed by the host cores (pi_sparse_ffn_hybrid), predictor first.
+    Eager steps (the call blocks the host), host clock around synchronised runs; one
+    host copy of the cold rows per layer instance, so no step finds the previous
+    instance's rows in the CPU caches."""
+    n_hot = layers[0].n_hot
+    rows = perm_np[n_hot:]
+    take = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a[rows]))  # noqa: E731
+    first = {k: take(getattr(L, k)) for k in ("W_up", "W_gate", "W_downT", "b_up", "b_gate")}
+    copies = [first] + [{k: None if v is None else v.clone() for k, v in first.items()}
+                        for _ in range(len(layers) - 1)]
+    act = layers[0].act
+    colds = [pb.make_part(wl.d, c["W_up"], c["W_downT"], act, c["W_gate"], c["b_up"], c["b_gate"],
+                          q4=wl.wdtype == "q4_0") for c in copies]
+    hots = [ly.parts()[0] for ly in layers]
+    preds = [ly.predictor() for ly in layers]
+    B = xs[0].shape[0]
+    y_cold = torch.zeros((B, wl.d), dtype=torch.float32, device=dev)
+    host_ws = torch.zeros(pb.pi_hybrid_host_bytes(wl.d, wl.n, B), dtype=torch.uint8,
+                          pin_memory=True)
+
+    def run(k, nthreads):
+        infos = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j, i in enumerate(idxs[:k]):
+            li = i % len(layers)
+            pb.pi_predict(preds[li], xs[i], buf.mask, None, None, buf.ws)
+            infos.append(pb.pi_sparse_ffn_hybrid(hots[li], colds[li], xs[i], buf.mask, buf.lists,
+                                                 y_cold, buf.y, buf.ws, host_ws, nthreads))
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / k, infos
+
+    def hot_only(k):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in idxs[:k]:
+            li = i % len(layers)
+            pb.pi_predict(preds[li], xs[i], buf.mask, None, None, buf.ws)
+            pb.pi_sparse_ffn_split(hots[li], None, xs[i], buf.lists, None, None, buf.y, buf.ws,
+                                   mask=buf.mask)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / k
+
+    # each timed run starts with the host caches holding none of the rows: a 512 MiB
+    # pass evicts them (the runs repeat the same steps)
+    flush = np.ones(64 << 20, np.float64)
+
+    def evict():
+        return float(flush.sum())
+
+    K = len(idxs)
+    run(K, threads)                              # warm the pool, the code, the page tables
+    evict()
+    us, infos = run(K, threads)
+    sweep = {}
+    for t in sorted({1, 4, 8, threads}):
+        if t <= threads:
+            evict()
+            u, inf = run(K, t)
+            sweep[str(t)] = {"us_per_step": round(u, 1),
+                             "host_us": round(float(np.mean([q.host_us for q in inf])), 1)}
+    del flush
+    hot_us = hot_only(K)
+    cold = np.array([q.cold_count for q in infos], np.float64)
+    cold_bytes = float(cold.mean()) * ((3 if wl.act == "reglu" else 2) * wrow_bytes(wl) + 4)
+    host_us = float(np.mean([q.host_us for q in infos]))
+    return {"n_hot": n_hot, "threads": threads, "us_per_step": round(us, 1),
+            "mean_cold_active": round(float(cold.mean()), 1),
+            "host_us": round(host_us, 1),
+            "host_us_p50": round(float(np.median([q.host_us for q in infos])), 1),
+            "host_wait_us": round(float(np.mean([q.wait_us for q in infos])), 1),
+            "host_gbps_cold_rows": round(cold_bytes / (host_us * 1e-6) / 1e9, 1),
+            "gpu_hot_only_us_eager": round(hot_us, 1),
+            "threads_sweep": sweep,
+            "hbm_bytes_saved": int((wl.n - n_hot) * ((3 if wl.act == "reglu" else 2)
+                                                     * wrow_bytes(wl) + 4)),
+            "timing": "eager, host clock; predictor + hybrid call per step"}
+
+
 def cpu_baseline(wl, L, n_hot, B, budget_s=8.0):
     """The oracle's layer step (predict, compact, sparse FFN per partition, merge) on the
     host: once single-threaded and once with its outer loops on all the cores this process
@@ -621,6 +703,10 @@ def main():
         if B == 1 and not args.cold_host and wl.xdtype == "f16":
             log("[bench] prompt-phase crossover over batches ...")
             extras["prompt_crossover"] = prompt_crossover(pb, torch, S, StepBuffers, wl, base, dev)
+        if wl.hot_frac is not None and not args.cold_host and B == 1:
+            log("[bench] hybrid step: cold partition on the host cores ...")
+            extras["hybrid_cpu_cold"] = hybrid_cpu_cold(pb, torch, wl, L, perm_np, layers, buf, xs,
+                                                        list(range(W, W + K)), dev, host_cpu()[2])
         if wl.hot_frac is not None and not args.cold_host:
             log("[bench] adaptive predictor threshold ...")
             extras["adaptive_predictor"] = adaptive_predictor(pb, torch, S, wl, base, buf, xs,

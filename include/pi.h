@@ -20,7 +20,8 @@
  *    [host].  The library never allocates, frees or retains caller memory.
  *  - Every call only enqueues work on `stream` (a hipStream_t passed as
  *    void*, NULL = the default stream) and returns; no call synchronises
- *    the host except pi_kernel_timer_stop.
+ *    the host except pi_kernel_timer_stop and the two calls that compute on
+ *    the host cores (pi_host_sparse_ffn, pi_sparse_ffn_hybrid).
  *  - Arguments are validated before anything is enqueued; on an error the
  *    call enqueues nothing and returns a nonzero pi_status.  pi_last_error()
  *    then holds a message (thread-local).
@@ -312,6 +313,80 @@ pi_status pi_calibrate_threshold(const pi_predictor* p, const pi_ffn_part* part,
  */
 pi_status pi_true_mask(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
                        uint64_t* mask, void* stream);
+
+/*
+ * The cold partition computed by the host cores (CSDN article, section on the
+ * CPU/GPU hybrid design and its figure; hada.io README summary,
+ * hybrid-approach section: the cold neurons stay in host memory and the CPU
+ * computes the predicted ones among them while the GPU computes the hot ones;
+ * the partial results are merged).
+ *
+ * pi_host_sparse_ffn: the sparse FFN of one partition on the CPU, every
+ * pointer a [host] pointer (part's weights and biases, x, idx, y):
+ *   y[b][:] = sum over idx[0 .. count) of h_bi * W_downT[i][:]
+ * with h as in pi_ffn_part, accumulated in float32.  x [B][d] PI_F32 or
+ * PI_F16; idx int32, ids outside 0..part->rows-1 add nothing; y [B][d]
+ * float32, overwritten.  Layouts as for the device calls (Q4_0 rows
+ * included); no alignment is required.  The work runs on a pool of host
+ * threads the library starts on first use (one per CPU the process may run
+ * on, at most 64): `threads` of them (0 = all); each takes a contiguous run of
+ * the list and the per-thread partials are added in a fixed order, so the
+ * result is reproducible for a given thread count.  Calls are serialised.
+ * Synchronous; uses no GPU.  Errors: PI_ERR_ARG / PI_ERR_DTYPE / PI_ERR_SHAPE
+ * as for pi_sparse_ffn (B in 1..PI_MAX_BATCH, count >= 0, threads >= 0).
+ */
+pi_status pi_host_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                             const int32_t* idx, int32_t count, float* y, int32_t threads);
+
+/* Host-side record of one pi_sparse_ffn_hybrid call. */
+typedef struct pi_hybrid_info {
+    int32_t cold_count;   /* predicted cold neurons the host computed */
+    int32_t threads;      /* host threads used */
+    double wait_us;       /* host wait for the mask and x to reach host memory */
+    double host_us;       /* host FFN time (list + rows + partial sums) */
+} pi_hybrid_info;
+
+/*
+ * Bytes of pinned host workspace pi_sparse_ffn_hybrid needs for a layer of n
+ * neurons, width d and batches up to B (0 if out of range).
+ */
+size_t pi_hybrid_host_bytes(int32_t d, int32_t n, int32_t B);
+
+/*
+ * One hybrid FFN step: hot partition on the GPU, cold partition on the host
+ * cores, at the same time, then merged on the GPU.
+ *   hot    partition in device memory (rows may be 0);
+ *   cold   partition whose weights and biases are in host memory (rows may
+ *          be 0); same d, wdtype and act as hot;
+ *   x      [B][d] device (PI_F32 or PI_F16), mask as written by pi_predict for
+ *          the n = hot rows + cold rows neurons (device);
+ *   lists  device, n_hot == hot->rows: receives the hot list and counts[0] as
+ *          pi_sparse_ffn_split writes them (nothing when hot has no rows);
+ *          the cold list is formed on the host (cold_idx and counts[1] are not
+ *          written);
+ *   y_cold [B][d] float32 device, out: the host's partial;
+ *   y      [B][d] float32 device, out: hot partial + y_cold;
+ *   ws     device workspace as for pi_sparse_ffn_split;
+ *   host_ws pinned host memory (hipHostMalloc), 64-byte aligned, of at least
+ *          pi_hybrid_host_bytes(d, n, B) bytes;
+ *   threads host threads for the cold rows (0 = all of the pool);
+ *   info   [host] optional record of the call.
+ * Order of work: mask and x are copied to host_ws on `stream`, the hot FFN is
+ * enqueued behind them, the host waits for the copies only, computes the cold
+ * rows (pi_host_sparse_ffn) while the GPU runs the hot ones, then enqueues
+ * the copy of its partial to y_cold and the merge.  Unlike the other calls
+ * this one blocks the host until the copies of mask and x are done and the
+ * host part is computed; it returns with the copy and the merge enqueued.
+ * The host workspace must not be reused from another stream or thread until
+ * this stream has passed the merge.  Not capturable in a HIP graph.  Errors
+ * are detected before anything is enqueued (host_ws not pinned and cold
+ * weights in device memory included: PI_ERR_ARG).
+ */
+pi_status pi_sparse_ffn_hybrid(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                               int32_t B, int32_t xdtype, const uint64_t* mask,
+                               const pi_active_lists* lists, float* y_cold, float* y, void* ws,
+                               size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                               int32_t threads, pi_hybrid_info* info, void* stream);
 
 /*
  * Hot/cold split from the tiers' read rates and the capacity budget (CSDN

@@ -32,6 +32,7 @@ EXPORTS = ("pi_workspace_bytes", "pi_workspace_init", "pi_predict", "pi_compact_
            "pi_dense_ffn",
            "pi_profile_counts", "pi_build_neuron_index", "pi_plan_hot_split",
            "pi_calibrate_workspace_bytes", "pi_calibrate_threshold", "pi_true_mask",
+           "pi_host_sparse_ffn", "pi_hybrid_host_bytes", "pi_sparse_ffn_hybrid",
            "pi_accumulate_mask", "pi_permute_rows",
            "pi_copy", "pi_stream_read",
            "pi_kernel_timer_start", "pi_kernel_timer_stop", "pi_kernel_name", "pi_status_string",
@@ -42,6 +43,11 @@ class PiError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{msg} (status {status})")
         self.status = status
+
+
+class HybridInfo(C.Structure):
+    _fields_ = [("cold_count", C.c_int32), ("threads", C.c_int32), ("wait_us", C.c_double),
+                ("host_us", C.c_double)]
 
 
 class Predictor(C.Structure):
@@ -91,6 +97,9 @@ def lib() -> C.CDLL:
         "pi_calibrate_workspace_bytes": ([I32, I32, I32, I32], SZ),
         "pi_calibrate_threshold": ([P, P, P, I32, I32, C.c_double, P, P, P, SZ, P], I32),
         "pi_true_mask": ([P, P, I32, I32, P, P], I32),
+        "pi_host_sparse_ffn": ([P, P, I32, I32, P, I32, P, I32], I32),
+        "pi_hybrid_host_bytes": ([I32, I32, I32], SZ),
+        "pi_sparse_ffn_hybrid": ([P, P, P, I32, I32, P, P, P, P, P, SZ, P, SZ, I32, P, P], I32),
         "pi_accumulate_mask": ([P, I32, P, P], I32),
         "pi_permute_rows": ([P, P, P, I32, I64, P], I32),
         "pi_copy": ([P, P, I64, P], I32),
@@ -254,6 +263,29 @@ def pi_calibrate_threshold(pred: Predictor, part: FfnPart, X, target_recall: flo
 def pi_true_mask(part: FfnPart, x, mask, stream=None):
     _check(lib().pi_true_mask(C.byref(part), ptr(x), x.shape[0], dtype_code(x), ptr(mask),
                               stream_handle(stream)))
+
+
+def pi_host_sparse_ffn(part: FfnPart, x, idx, count: int, y, threads: int = 0):
+    """Every tensor here is a CPU tensor (host memory); runs on the host cores."""
+    _check(lib().pi_host_sparse_ffn(C.byref(part), ptr(x), x.shape[0], dtype_code(x), ptr(idx),
+                                    int(count), ptr(y), int(threads)))
+
+
+def pi_hybrid_host_bytes(d: int, n: int, B: int) -> int:
+    return lib().pi_hybrid_host_bytes(d, n, B)
+
+
+def pi_sparse_ffn_hybrid(hot: FfnPart, cold: FfnPart, x, mask, lists: ActiveLists, y_cold, y, ws,
+                         host_ws, threads: int = 0, stream=None) -> HybridInfo:
+    """hot on the device, cold (host-memory weights) on the host cores; host_ws is a pinned
+    CPU tensor of at least pi_hybrid_host_bytes bytes.  Returns the call's HybridInfo."""
+    info = HybridInfo()
+    _check(lib().pi_sparse_ffn_hybrid(C.byref(hot), C.byref(cold), ptr(x), x.shape[0],
+                                      dtype_code(x), ptr(mask), C.byref(lists), ptr(y_cold),
+                                      ptr(y), ptr(ws), ws.numel() * ws.element_size(),
+                                      ptr(host_ws), host_ws.numel() * host_ws.element_size(),
+                                      int(threads), C.byref(info), stream_handle(stream)))
+    return info
 
 
 def pi_accumulate_mask(mask, n: int, counts, stream=None):

@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <chrono>
 
 #include <cstdarg>
 #include <cstdio>
@@ -13,6 +14,7 @@
 
 #include "pi.h"
 #include "pi_ffn.h"
+#include "pi_host.h"
 #include "pi_kernels.h"
 #include "pi_mfma.h"
 
@@ -191,6 +193,65 @@ pi_status scratch_ptr(hipStream_t s, void** out) {
     }
     *out = g_scratch_ptr[dev];
     return PI_OK;
+}
+
+// ---- host side of the hybrid step --------------------------------------------------
+// One event per device (created on first use) marks the arrival of mask and x in
+// the host workspace; the host spins on it, then computes.
+std::mutex g_event_mu;
+hipEvent_t g_arrive[MAX_DEVICES] = {};
+
+pi_status arrival_event(hipStream_t s, hipEvent_t* out) {
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PI_ERR_HIP, "stream device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(PI_ERR_HIP, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_event_mu);
+    if (!g_arrive[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&g_arrive[dev], hipEventDisableTiming);
+        if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess) {
+            g_arrive[dev] = nullptr;
+            return fail(PI_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        }
+    }
+    *out = g_arrive[dev];
+    return PI_OK;
+}
+
+// Where a pointer lives, as the runtime reports it; Unregistered for memory it
+// does not know (ordinary pageable host memory).  Clears the error an unknown
+// pointer may leave.
+hipMemoryType memory_type(const void* p) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return hipMemoryTypeUnregistered;
+    }
+    return a.type;
+}
+
+size_t align64(size_t v) { return (v + 63) & ~size_t(63); }
+
+// host workspace of the hybrid step: mask words, x, the host's partial of y, the cold ids
+size_t hybrid_host_layout(int d, int n, int B, size_t off[4]) {
+    size_t o = 0;
+    off[0] = o;
+    o = align64(o + (size_t)((n + 63) / 64) * 8);
+    off[1] = o;
+    o = align64(o + (size_t)B * d * 4);
+    off[2] = o;
+    o = align64(o + (size_t)B * d * 4);
+    off[3] = o;
+    o = align64(o + (size_t)n * 4);
+    return o;
+}
+
+double us_since(const std::chrono::steady_clock::time_point& t0) {
+    return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
 }
 
 // ---- argument checks ----------------------------------------------------------------
@@ -453,7 +514,8 @@ pi_status run_ffn(const FfnArgs& a, const DownOut& o, int wt, int xt, int act, i
 pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x, int B,
                      int xdtype, const uint64_t* mask, const int32_t* idx0, const int32_t* idx1,
                      const int32_t* counts, bool dense, float* y0, float* y1, float* y, void* ws,
-                     size_t ws_bytes, hipStream_t s, bool static_ws = false, int dense_from = 0) {
+                     size_t ws_bytes, hipStream_t s, bool static_ws = false, int dense_from = 0,
+                     bool check_only = false) {
     TRY(check_part(hot, "hot", !dense));
     const bool has_cold = cold && cold->rows > 0;
     if (cold) TRY(check_part(cold, "cold", true));
@@ -488,6 +550,8 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
         ws_bytes = PI_SCRATCH_BYTES;
     }
     TRY(check_ws(ws, ws_bytes, ws_ffn_bytes(d, n, B, nch)));
+    if (mask) CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
+    if (check_only) return PI_OK;
 
     uint8_t* base = static_cast<uint8_t*>(ws);
     FfnArgs a{};
@@ -510,7 +574,6 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.rows[0] = hot->rows;
     a.rows[1] = has_cold ? cold->rows : 0;
     if (mask) {
-        CHECK(aligned(mask, 8), PI_ERR_ALIGN, "mask must be 8-byte aligned");
         Lists L{hot->rows, const_cast<int32_t*>(idx0), const_cast<int32_t*>(idx1),
                 const_cast<int32_t*>(counts)};
         if ((n + 63) / 64 <= (fused ? FUSED_MASK_WORDS : MASK_WORDS_MAX)) {
@@ -905,6 +968,115 @@ pi_status pi_true_mask(const pi_ffn_part* part, const void* x, int32_t B, int32_
     if (wt == F16) return xdtype == F32 ? TM(F16, F32) : TM(F16, F16);
     return xdtype == F32 ? TM(Q4, F32) : TM(Q4, F16);
 #undef TM
+}
+
+pi_status pi_host_sparse_ffn(const pi_ffn_part* part, const void* x, int32_t B, int32_t xdtype,
+                             const int32_t* idx, int32_t count, float* y, int32_t threads) {
+    TRY(check_part(part, "part", true));
+    TRY(check_dtype_x(xdtype));
+    CHECK(B >= 1 && B <= PI_MAX_BATCH, PI_ERR_SHAPE, "B must be in 1..%d", PI_MAX_BATCH);
+    CHECK(x && y, PI_ERR_ARG, "x and y required");
+    CHECK(count >= 0, PI_ERR_SHAPE, "count must be >= 0");
+    CHECK(count == 0 || idx, PI_ERR_ARG, "idx required for count > 0");
+    CHECK(threads >= 0, PI_ERR_ARG, "threads must be >= 0");
+    host::sparse_ffn(*part, x, B, xdtype, idx, part->rows > 0 ? count : 0, y, threads);
+    return PI_OK;
+}
+
+size_t pi_hybrid_host_bytes(int32_t d, int32_t n, int32_t B) {
+    if (d <= 0 || n <= 0 || n > (1 << 24) || B <= 0 || B > PI_MAX_BATCH) return 0;
+    size_t off[4];
+    return hybrid_host_layout(d, n, B, off);
+}
+
+pi_status pi_sparse_ffn_hybrid(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
+                               int32_t B, int32_t xdtype, const uint64_t* mask,
+                               const pi_active_lists* lists, float* y_cold, float* y, void* ws,
+                               size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                               int32_t threads, pi_hybrid_info* info, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    TRY(check_part(hot, "hot", true));
+    CHECK(cold, PI_ERR_ARG, "cold partition required (it may have 0 rows)");
+    TRY(check_part(cold, "cold", true));
+    CHECK(cold->d == hot->d && cold->wdtype == hot->wdtype && cold->act == hot->act, PI_ERR_SHAPE,
+          "hot and cold partitions differ in d, wdtype or act");
+    TRY(check_dtype_x(xdtype));
+    CHECK(B >= 1 && B <= PI_MAX_BATCH, PI_ERR_SHAPE, "B must be in 1..%d", PI_MAX_BATCH);
+    CHECK(x && aligned(x, 16), x ? PI_ERR_ALIGN : PI_ERR_ARG, "x must be non-NULL and 16-byte aligned");
+    CHECK(mask && aligned(mask, 8), mask ? PI_ERR_ALIGN : PI_ERR_ARG, "mask must be non-NULL and 8-byte aligned");
+    CHECK(lists && lists->n_hot == hot->rows, PI_ERR_SHAPE, "lists required with n_hot == hot->rows");
+    CHECK(y_cold && y && aligned(y_cold, 16) && aligned(y, 16), PI_ERR_ARG,
+          "y_cold and y required (16-byte aligned)");
+    CHECK(threads >= 0, PI_ERR_ARG, "threads must be >= 0");
+    const int d = hot->d;
+    const int64_t n64 = (int64_t)hot->rows + cold->rows;
+    CHECK(n64 >= 1 && n64 <= (1 << 24), PI_ERR_SHAPE, "hot rows + cold rows must be in 1..2^24");
+    const int n = (int)n64;
+    size_t off[4];
+    const size_t hneed = hybrid_host_layout(d, n, B, off);
+    CHECK(host_ws && aligned(host_ws, 64), PI_ERR_ARG, "host_ws required (64-byte aligned)");
+    CHECK(host_ws_bytes >= hneed, PI_ERR_WORKSPACE, "host_ws has %zu bytes, needs %zu", host_ws_bytes, hneed);
+    CHECK(memory_type(host_ws) == hipMemoryTypeHost, PI_ERR_ARG, "host_ws must be pinned host memory (hipHostMalloc)");
+    if (cold->rows > 0) {
+        const void* w[3] = {cold->W_up, cold->W_downT, cold->act == PI_REGLU ? cold->W_gate : nullptr};
+        for (const void* p : w)
+            CHECK(!p || memory_type(p) != hipMemoryTypeDevice, PI_ERR_ARG,
+                  "cold weights must be in host memory (the host cores read them)");
+        const float* b[2] = {cold->b_up, cold->b_gate};
+        for (const float* p : b)
+            CHECK(!p || memory_type(p) != hipMemoryTypeDevice, PI_ERR_ARG, "cold biases must be in host memory");
+    }
+    if (hot->rows > 0)
+        TRY(ffn_common(hot, nullptr, x, B, xdtype, mask, lists->hot_idx, nullptr, lists->counts, false, nullptr,
+                       nullptr, y, ws, ws_bytes, s, false, 0, /*check_only=*/true));
+    hipEvent_t arrive;
+    TRY(arrival_event(s, &arrive));
+
+    // the device's address of the host workspace (pinned memory is mapped for the GPU)
+    void* hdev = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&hdev, host_ws, 0);
+    if (e != hipSuccess || !hdev) {
+        (void)hipGetLastError();
+        return fail(PI_ERR_ARG, "host_ws is not mapped for the device (allocate it with hipHostMalloc)");
+    }
+    uint8_t* hd = static_cast<uint8_t*>(hdev);
+
+    // 1. mask and x to host memory, then the hot partition behind them on the GPU
+    uint8_t* hb = static_cast<uint8_t*>(host_ws);
+    const int words = (n + 63) / 64;
+    const int x16 = (int)((size_t)B * d * (xdtype == PI_F32 ? 4 : 2) / 16);
+    TRY(launch(PI_K_MERGE, k_export, dim3((std::max(words, x16) + THREADS - 1) / THREADS), dim3(THREADS), 0, s,
+               mask, words, (const uint4*)x, x16, (uint64_t*)(hd + off[0]), (uint4*)(hd + off[1])));
+    e = hipEventRecord(arrive, s);
+    if (e != hipSuccess) return fail(PI_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    if (hot->rows > 0)
+        TRY(ffn_common(hot, nullptr, x, B, xdtype, mask, lists->hot_idx, nullptr, lists->counts, false, nullptr,
+                       nullptr, y, ws, ws_bytes, s));
+
+    // 2. the cold partition on the host cores while the GPU runs the hot one
+    const auto t0 = std::chrono::steady_clock::now();
+    e = hipEventSynchronize(arrive);
+    if (e != hipSuccess) return fail(PI_ERR_HIP, "waiting for mask and x: %s", hipGetErrorString(e));
+    const double wait_us = us_since(t0);
+    const auto t1 = std::chrono::steady_clock::now();
+    int32_t* ids = reinterpret_cast<int32_t*>(hb + off[3]);
+    float* yc = reinterpret_cast<float*>(hb + off[2]);
+    const int count = cold->rows > 0 ? host::cold_list(reinterpret_cast<const uint64_t*>(hb + off[0]), hot->rows, n, ids) : 0;
+    host::sparse_ffn(*cold, hb + off[1], B, xdtype, ids, count, yc, threads);
+    const double host_us = us_since(t1);
+    if (info) {
+        info->cold_count = count;
+        info->threads = std::max(1, std::min({threads > 0 ? threads : host::threads_available(),
+                                               host::threads_available(), std::max(count, 1)}));
+        info->wait_us = wait_us;
+        info->host_us = host_us;
+    }
+
+    // 3. y_cold = the host's partial (read from host memory), y = hot partial + y_cold
+    const int64_t len4 = (int64_t)B * d / 4;
+    const int grid = (int)std::min<int64_t>((len4 + THREADS - 1) / THREADS, 1024);
+    return launch(PI_K_MERGE, k_merge_host, dim3(grid), dim3(THREADS), 0, s, (const float4*)(hd + off[2]), len4,
+                  hot->rows > 0, (float4*)y_cold, (float4*)y);
 }
 
 pi_status pi_accumulate_mask(const uint64_t* mask, int32_t n, uint32_t* counts, void* stream) {

@@ -701,6 +701,40 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ a,
 }
 
 // ===========================================================================
+// Hybrid step, the two ends of the host's share.
+// k_export: the predicted mask words and x, written straight into the host
+// workspace (pinned host memory) for the host cores to read.
+// k_merge_host: the host's partial of y, read straight from pinned host
+// memory: y_cold = host partial, y = (y_hot or 0) + host partial.  len and the
+// x bytes are multiples of 16 bytes (d % 64 == 0).
+// ===========================================================================
+__global__ __launch_bounds__(THREADS) void k_export(const uint64_t* __restrict__ mask, int words,
+                                                    const uint4* __restrict__ x, int x16,
+                                                    uint64_t* __restrict__ mask_out,
+                                                    uint4* __restrict__ x_out) {
+    const int i = blockIdx.x * THREADS + threadIdx.x;
+    if (i < words) mask_out[i] = mask[i];
+    if (i < x16) x_out[i] = x[i];
+}
+
+__global__ __launch_bounds__(THREADS) void k_merge_host(const float4* __restrict__ host_part,
+                                                        int64_t len4, bool has_hot,
+                                                        float4* __restrict__ y_cold,
+                                                        float4* __restrict__ y) {
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < len4; i += stride) {
+        const float4 c = host_part[i];
+        y_cold[i] = c;
+        if (has_hot) {
+            const float4 h = y[i];
+            y[i] = make_float4(h.x + c.x, h.y + c.y, h.z + c.z, h.w + c.w);
+        } else {
+            y[i] = c;
+        }
+    }
+}
+
+// ===========================================================================
 // Offline profiling: counts[i] = #{s : pre_i(X_s) > 0}.  One wave per row,
 // samples in groups of BT.  (Offline, not on the decode path.)
 // ===========================================================================

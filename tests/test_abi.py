@@ -200,3 +200,32 @@ def test_calibrate_and_true_mask_validation(L):
     assert L.pi_true_mask(C.byref(part), FAKE, 0, pb.PI_F16, FAKE, None) == pb.PI_ERR_SHAPE
     assert L.pi_true_mask(C.byref(part), FAKE, 1, pb.PI_F16, FAKE + 4, None) == pb.PI_ERR_ARG
     assert L.pi_true_mask(C.byref(_part(d=100)), FAKE, 1, pb.PI_F16, FAKE, None) == pb.PI_ERR_SHAPE
+
+
+def test_hybrid_validation(L):
+    """pi_sparse_ffn_hybrid rejects bad arguments before any runtime call."""
+    assert L.pi_hybrid_host_bytes(0, 100, 1) == 0
+    assert L.pi_hybrid_host_bytes(256, 100, pb.PI_MAX_BATCH + 1) == 0
+    hb = L.pi_hybrid_host_bytes(256, 100, 2)
+    # mask words, x and the host partial (fp32 [B][d] each), the cold ids; 64-byte runs
+    assert hb >= 2 * 8 + 2 * 256 * 4 * 2 + 100 * 4 and hb % 64 == 0
+    hot, cold = _part(rows=60), _part(rows=40)
+    lists = pb.ActiveLists(60, FAKE, FAKE, FAKE)
+
+    def hyb(h=hot, c=cold, B=1, xdt=pb.PI_F16, mask=FAKE, li=lists, yc=FAKE, y=FAKE, hws=FAKE,
+            hn=hb, threads=0):
+        return L.pi_sparse_ffn_hybrid(C.byref(h), None if c is None else C.byref(c), FAKE, B, xdt,
+                                      mask, None if li is None else C.byref(li), yc, y, FAKE,
+                                      1 << 20, hws, hn, threads, None, None)
+    assert hyb(c=None) == pb.PI_ERR_ARG
+    assert hyb(c=_part(rows=40, d=512)) == pb.PI_ERR_SHAPE
+    assert hyb(B=0) == pb.PI_ERR_SHAPE
+    assert hyb(xdt=pb.PI_Q4_0) == pb.PI_ERR_DTYPE
+    assert hyb(mask=None) == pb.PI_ERR_ARG
+    assert hyb(mask=FAKE + 4) == pb.PI_ERR_ALIGN
+    assert hyb(li=pb.ActiveLists(59, FAKE, FAKE, FAKE)) == pb.PI_ERR_SHAPE
+    assert hyb(yc=None) == pb.PI_ERR_ARG
+    assert hyb(threads=-1) == pb.PI_ERR_ARG
+    assert hyb(hws=None) == pb.PI_ERR_ARG
+    assert hyb(hws=FAKE + 32) == pb.PI_ERR_ARG
+    assert hyb(hn=L.pi_hybrid_host_bytes(256, 100, 1) - 64) == pb.PI_ERR_WORKSPACE
