@@ -76,6 +76,7 @@ def kernel_bytes(wl, B, active):
         "k_down": active * (wrow_bytes(wl) + 4) + 4 * B * active,
         "k_ffn": active * (m_up * wrow_bytes(wl) + wrow_bytes(wl) + 4) + B * wl.d * ex,
         "k_reduce": 4 * B * wl.d,
+        "k_up_finish": 0,        # sum of the up kernel's K slices: implementation traffic only
     }
 
 
@@ -632,7 +633,7 @@ def main():
     # active count of each step (deterministic, so identical to the first pass)
     kids = {"k_pred_l1": pb.PI_K_PRED_L1, "k_pred_l2": pb.PI_K_PRED_L2,
             "k_compact": pb.PI_K_COMPACT, "k_up": pb.PI_K_UP, "k_down": pb.PI_K_DOWN,
-            "k_ffn": pb.PI_K_FFN, "k_reduce": pb.PI_K_REDUCE}
+            "k_ffn": pb.PI_K_FFN, "k_reduce": pb.PI_K_REDUCE, "k_up_finish": pb.PI_K_UP_FINISH}
     for kid in kids.values():
         pb.pi_kernel_timer_start(kid, 2 * K)
     active = []

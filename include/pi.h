@@ -463,7 +463,8 @@ enum {
     PI_K_FFN = 10,        /* fused compaction + up/gate + activation + down (batch <= 4) */
     PI_K_ACCUMULATE = 11, /* online activation counts from a mask */
     PI_K_STREAM = 12,     /* plain read stream (attainable bandwidth) */
-    PI_K_COUNT = 13
+    PI_K_UP_FINISH = 13,  /* sum of the up kernel's K slices + activation (batch >= 2) */
+    PI_K_COUNT = 14
 };
 
 /*

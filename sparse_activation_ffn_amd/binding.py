@@ -21,7 +21,8 @@ PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
 PI_RELU, PI_REGLU, PI_SQRELU = 0, 1, 2
 PI_MAX_BATCH = 64
 (PI_K_PRED_L1, PI_K_PRED_L2, PI_K_COMPACT, PI_K_UP, PI_K_DOWN, PI_K_MERGE, PI_K_PROFILE,
- PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_STREAM, PI_K_COUNT) = range(14)
+ PI_K_INDEX, PI_K_COPY, PI_K_REDUCE, PI_K_FFN, PI_K_ACCUMULATE, PI_K_STREAM, PI_K_UP_FINISH,
+ PI_K_COUNT) = range(15)
 PI_STREAM_SINK_WORDS = 2048
 PI_SCRATCH_BYTES = 32 << 20
 

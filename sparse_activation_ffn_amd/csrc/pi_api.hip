@@ -133,9 +133,31 @@ size_t ws_h_bytes(int n, int B) {
     return align256(f32 > f16 ? f32 : f16);
 }
 
-// h and the partials of y
+// Split of the matrix-core up kernel over K, for Q4_0 weights at batches of up
+// to 16 (one 16-token tile): there the active tiles alone leave the compute
+// units short of work (OPT-175B-shaped layer, batch 8: about 235 tiles of 64
+// items for 256 CUs that hold 4 such workgroups each); four slices took the
+// step from 141 to 133 us.  Measured no gain at batch 64 (the tiles already
+// fill the chip; 315 -> 323 us with two slices) nor for f16 weights at batch 4
+// (ReGLU-70B-shaped layer 132 -> 139 us), so those run unsplit.
+constexpr int UP_SPLIT_SMALL_B = 4;
+constexpr int UP_SPLIT_MAX_B = 16;
+int up_split_want(int B, int wt) { return wt == Q4 && B <= UP_SPLIT_MAX_B ? UP_SPLIT_SMALL_B : 1; }
+int64_t up_part_ld(int n) { return (int64_t)(n + 63) / 64 * 64; }
+
+// the partials of y (down kernels), which the split up kernel's partials share
+size_t ws_part_bytes(int d, int n, int B, int nparts) {
+    size_t v = (size_t)nparts * B * d * 4;
+    if (B >= MFMA_MIN_BATCH && B <= UP_SPLIT_MAX_B) {
+        const size_t u = (size_t)UP_SPLIT_SMALL_B * B * up_part_ld(n) * 4;
+        if (u > v) v = u;
+    }
+    return align256(v);
+}
+
+// h and the partials
 size_t ws_ffn_bytes(int d, int n, int B, int nparts) {
-    return WS_CTR_BYTES + ws_h_bytes(n, B) + align256((size_t)nparts * B * d * 4);
+    return WS_CTR_BYTES + ws_h_bytes(n, B) + ws_part_bytes(d, n, B, nparts);
 }
 
 // ---- timing hooks --------------------------------------------------------------
@@ -459,13 +481,20 @@ pi_status launch_up_kernel(K kern, const FfnArgs& a, int rows_cap, hipStream_t s
     const int grid = rows_cap > 0 ? (rows_cap + UR - 1) / UR : 1;
     const size_t sh = a.mask ? (size_t)(a.n + 63) / 64 * 8 : 0;   // mask words
     TRY(allow_lds(kern, sh));
-    return launch(PI_K_UP, kern, dim3(grid), dim3(MFMA_WG), sh, s, a,
+    return launch(PI_K_UP, kern, dim3(grid, a.ksplit > 1 ? a.ksplit : 1), dim3(MFMA_WG), sh, s, a,
                   reinterpret_cast<_Float16*>(a.h));
 }
 
 template <int WT, int ACT, int MT>
 pi_status launch_mfma_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
-    return launch_up_kernel(k_mfma_up<WT, ACT, MT, 1>, a, rows_cap, s);
+    TRY(launch_up_kernel(k_mfma_up<WT, ACT, MT, 1>, a, rows_cap, s));
+    if (a.ksplit <= 1) return PI_OK;
+    // the slices' sum and the activation (item count from the device)
+    constexpr int NM = ACT == REGLU ? 2 : 1;
+    const int gx = std::max(1, std::min((rows_cap + THREADS - 1) / THREADS, 64));
+    return launch(PI_K_UP_FINISH, k_up_finish<ACT, NM>, dim3(gx, a.B), dim3(THREADS), 0, s,
+                  (const float*)a.upart, a.ksplit, a.upart_ld, a.B, (const int*)a.up_ht,
+                  reinterpret_cast<_Float16*>(a.h), a.h_ld);
 }
 
 template <int WT, int ACT>
@@ -598,6 +627,17 @@ pi_status ffn_common(const pi_ffn_part* hot, const pi_ffn_part* cold, const void
     a.h_ld = mfma ? mfma_h_ld(n) : (n > 0 ? n : 1);
     DownOut o{};
     o.partials = reinterpret_cast<float*>(base + WS_CTR_BYTES + ws_h_bytes(n, B));
+    a.ksplit = 1;
+    if (mfma) {
+        // slices of the up kernel: as many as wanted that the partial region holds
+        const int nm = hot->act == PI_REGLU ? 2 : 1;
+        const int64_t per = (int64_t)nm * B * up_part_ld(n) * 4;
+        const int64_t fit = (int64_t)ws_part_bytes(d, n, B, nch) / per;
+        a.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(up_split_want(B, wt), fit));
+        a.upart = o.partials;
+        a.upart_ld = (int)up_part_ld(n);
+        a.up_ht = reinterpret_cast<int*>(base);
+    }
     o.y_part[0] = y0;
     o.y_part[1] = y1;
     o.y = y;
@@ -667,7 +707,8 @@ const char* pi_last_error(void) { return g_err; }
 const char* pi_kernel_name(int32_t kid) {
     static const char* names[PI_K_COUNT] = {"k_pred_l1", "k_pred_l2", "k_compact", "k_up", "k_down",
                                             "k_merge", "k_profile", "k_index", "k_copy", "k_reduce",
-                                            "k_ffn", "k_accumulate_mask", "k_stream_read"};
+                                            "k_ffn", "k_accumulate_mask", "k_stream_read",
+                                            "k_up_finish"};
     return (kid >= 0 && kid < PI_K_COUNT) ? names[kid] : "?";
 }
 

@@ -264,6 +264,14 @@ struct FfnArgs {
     // prompt-phase crossover to the dense FFN); the lists and counts still
     // describe the predicted set
     int dense_from;
+    // matrix-core up kernel split over K (ksplit > 1): slice k of every tile
+    // writes its fp32 pre-activations (bias added by slice 0) to
+    // upart[((k NM + g) B + token) upart_ld + item]; up_ht receives H and the
+    // item count T, and k_up_finish sums the slices and applies the activation
+    int ksplit;
+    float* upart;
+    int upart_ld;
+    int* up_ht;
 };
 
 // Largest mask (in 64-bit words) whose compaction k_up does in LDS.

@@ -215,7 +215,7 @@ __device__ __forceinline__ void up_task(int t, int& r, int& ch) {
 // Returns false (uniformly) when the workgroup has no items.
 template <int UR>
 __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, uint64_t* s_words,
-                           int& H, int& C) {
+                           int& H, int& C, bool lists_out = true) {
     __shared__ int s_cnt[2];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     bool dense;
@@ -255,7 +255,7 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
         __syncthreads();
         H = s_cnt[0];
         C = T - H;
-        if (blockIdx.x == 0 && tid == 0) {
+        if (lists_out && blockIdx.x == 0 && tid == 0) {
             a.out_counts[0] = H;
             a.out_counts[1] = C;
         }
@@ -279,7 +279,7 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
                         s_row[rank - i0] = (unsigned)row < (unsigned)a.rows[part] ? row : -1;
                         s_part[rank - i0] = part;
                     }
-                    a.out_idx[part][part == 0 ? rank : rank - H] = row;
+                    if (lists_out) a.out_idx[part][part == 0 ? rank : rank - H] = row;
                 }
             }
             r0 += pc;
@@ -349,6 +349,65 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const f4m (&acc)[N
     }
 }
 
+// Split over K: this slice's fp32 pre-activations of the tile (slice 0 adds
+// the biases), for k_up_finish.  Same lane mapping as up_epilogue.
+template <int NM, int NT, int MT>
+__device__ __forceinline__ void up_partials(const FfnArgs& a, const f4m (&acc)[NM][NT][MT], const int* s_row,
+                                            const int* s_part, int i0, int T, int slice) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int q = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int jn = 0; jn < NT; ++jn) {
+        const int r = 16 * NT * wv + 16 * jn + c;
+        const int row = s_row[r], part = s_part[r];
+        const int item = i0 + r;
+        if (item < T) {
+            float bias[NM];
+            bias[0] = (slice == 0 && row >= 0 && a.bup[part]) ? a.bup[part][row] : 0.0f;
+            if (NM == 2) bias[NM - 1] = (slice == 0 && row >= 0 && a.bgate[part]) ? a.bgate[part][row] : 0.0f;
+#pragma unroll
+            for (int g = 0; g < NM; ++g)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tok = 16 * mt + 4 * q + i;
+                        if (tok < a.B)
+                            a.upart[((int64_t)(slice * NM + g) * a.B + tok) * a.upart_ld + item] =
+                                acc[g][jn][mt][i] + bias[g];
+                    }
+        }
+    }
+}
+
+// The slices' sum, the activation and the f16 h write of every (token, item)
+// of the step (fixed slice order).  grid (x: item blocks, y: tokens).
+template <int ACT, int NM>
+__global__ __launch_bounds__(THREADS) void k_up_finish(const float* __restrict__ upart, int S, int ld, int B,
+                                                       const int* __restrict__ ht, _Float16* __restrict__ h16,
+                                                       int h_ld) {
+    const int H = ht[0], T = ht[1];
+    const int tok = blockIdx.y;
+    for (int item = blockIdx.x * THREADS + threadIdx.x; item < T; item += gridDim.x * THREADS) {
+        float v[NM];
+#pragma unroll
+        for (int g = 0; g < NM; ++g) v[g] = 0.0f;
+        for (int k = 0; k < S; ++k)
+#pragma unroll
+            for (int g = 0; g < NM; ++g) v[g] += upart[((int64_t)(k * NM + g) * B + tok) * ld + item];
+        float hv;
+        if (ACT == RELU) {
+            hv = v[0] > 0.0f ? v[0] : 0.0f;
+        } else if (ACT == SQRELU) {
+            const float r = v[0] > 0.0f ? v[0] : 0.0f;
+            hv = r * r;
+        } else {
+            hv = (v[NM - 1] > 0.0f ? v[NM - 1] : 0.0f) * v[0];
+        }
+        h16[(int64_t)tok * h_ld + h_pos(item, H)] = (_Float16)hv;
+    }
+}
+
 template <int WT, int ACT, int MT, int NT>
 __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __restrict__ h16) {
     constexpr int NM = ACT == REGLU ? 2 : 1;
@@ -363,8 +422,14 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
     const int q = lane >> 4, c = lane & 15;
     const int i0 = blockIdx.x * UR;
 
+    const int slice = blockIdx.y, nsl = a.ksplit;
     int H, C;
-    if (!up_resolve<UR>(a, i0, s_row, s_part, s_words, H, C)) return;
+    const bool any = up_resolve<UR>(a, i0, s_row, s_part, s_words, H, C, slice == 0);
+    if (nsl > 1 && blockIdx.x == 0 && slice == 0 && tid == 0) {
+        a.up_ht[0] = H;
+        a.up_ht[1] = H + C;
+    }
+    if (!any) return;
     const int T = H + C;
 
     // per-thread weight sources (a row that is not one, an out-of-range id,
@@ -475,8 +540,10 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
         __builtin_amdgcn_sched_group_barrier(0x100, NKS * (MT + NM * NT), 0);   // LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, NKS * NM * NT * MT, 0);     // matrix-core ops
     };
-    run_pipeline<D, Stage>(0, a.d / KS, load, store, compute);
-    up_epilogue<ACT, NM, NT, MT>(a, acc, s_row, s_part, i0, H, T, h16);
+    const int steps = a.d / KS;
+    run_pipeline<D, Stage>(steps * slice / nsl, steps * (slice + 1) / nsl, load, store, compute);
+    if (nsl > 1) up_partials<NM, NT, MT>(a, acc, s_row, s_part, i0, T, slice);
+    else up_epilogue<ACT, NM, NT, MT>(a, acc, s_row, s_part, i0, H, T, h16);
 }
 
 // Split of one partition's items over chunks, chunk starts on multiples of 8.
