@@ -19,6 +19,7 @@
 
 #include <immintrin.h>
 #include <sched.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <atomic>
@@ -114,8 +115,18 @@ int allowed_cpus() {
     return std::max(1, (int)std::thread::hardware_concurrency());
 }
 
+// The pool of this process.  A child created by fork() has none of its
+// parent's worker threads: it builds a pool of its own on first use (the
+// parent's copy is left alone).
 Pool& pool() {
-    static Pool* p = new Pool(std::min(allowed_cpus(), MAX_THREADS));
+    static std::mutex mu;
+    static Pool* p = nullptr;
+    static pid_t owner = 0;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!p || owner != getpid()) {
+        p = new Pool(std::min(allowed_cpus(), MAX_THREADS));
+        owner = getpid();
+    }
     return *p;
 }
 

@@ -157,3 +157,29 @@ def test_portable_code_path_matches_oracle():
                        timeout=600)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     assert " passed" in r.stdout
+
+
+def test_forked_child_builds_its_own_pool():
+    """A child forked after the pool exists (its worker threads are not copied) still
+    computes: it starts a pool of its own."""
+    import os
+    name = "f16-relu"
+    wl, (lo, hi) = CASES[name]
+    L = _layer(name)
+    part = _host_part(L, lo, hi)
+    x = S.make_x(wl, 0, 5, 2)
+    ids = _ids(hi - lo, seed=3)
+    want = _run(part, x, ids, threads=4)            # the parent's pool now exists
+    r, w = os.pipe()
+    pid = os.fork()
+    if pid == 0:                                    # child: same call, report bit equality
+        ok = False
+        try:
+            ok = np.array_equal(_run(part, x, ids, threads=4).view(np.uint32), want.view(np.uint32))
+        finally:
+            os.write(w, b"1" if ok else b"0")
+            os._exit(0)
+    os.close(w)
+    got = os.read(r, 1)
+    os.waitpid(pid, 0)
+    assert got == b"1"
