@@ -610,9 +610,12 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
     const int32_t* idx = part == 0 ? a.idx[0] : a.idx[1];
     const int prows = part == 0 ? a.rows[0] : a.rows[1];
     const int steps = (hi - lo + DK - 1) / DK;
-    // this thread's 8 x 8 weight block: rows 8 rg .. +7 of the step, columns 8 cg .. +7
-    const int cg = tid & 15, rg = tid >> 4;
-    const int col0 = c0 + 8 * cg;
+    // this thread's weights of a step.  f16: an 8 x 8 block, rows 8 rg .. +7,
+    // columns 8 cg .. +7.  Q4_0: rows 4 rg .. +3 and the 16 columns held by 8
+    // code bytes of one block (both nibbles of each byte: columns k .. k+7 and
+    // k+16 .. k+23 of the block, k = 0 or 8), so no code byte is loaded twice.
+    const int cg = WT == Q4 ? (tid & 7) : (tid & 15), rg = WT == Q4 ? (tid >> 3) : (tid >> 4);
+    const int col0 = WT == Q4 ? c0 + 32 * (cg >> 1) + 8 * (cg & 1) : c0 + 8 * cg;
     // Q4_0 rows are addressed by 32-bit offsets from the partition base (the host
     // keeps Q4_0 partitions on this path below 2 GiB): a base in scalar registers
     // plus a 32-bit offset is one load operand, instead of 64-bit arithmetic
@@ -622,6 +625,7 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
     gbyte* const wb = (gbyte*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(bu >> 32)) << 32) |
                                (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bu));
     const unsigned coff = 16u * (unsigned)(col0 >> 5) + (unsigned)(col0 & 15);      // 8 code bytes
+    constexpr int NR = WT == Q4 ? 4 : 8;                                             // rows per thread
     const unsigned soff = (unsigned)(a.d / 2) + 2u * (unsigned)(col0 >> 5);          // the block's scale
     f4m acc[2][MT];
 #pragma unroll
@@ -651,8 +655,8 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
             const int* ids = s_ids[s % (D + 1)];
             R.rows_ok = 0;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int row = ids[8 * rg + r];
+            for (int r = 0; r < NR; ++r) {
+                const int row = ids[NR * rg + r];
                 if (WT == Q4) {
                     // a non-row reads row 0 and gets a zero scale (zero weights)
                     R.rows_ok |= (row >= 0 ? 1u : 0u) << r;
@@ -678,25 +682,50 @@ __global__ __launch_bounds__(DOWN_WG) void k_mfma_down(FfnArgs a, DownOut o, con
             R.full = i0 + DK <= hi;
         };
         auto store = [&](const Stage& R, bool act) {
-            unsigned V[8][4];                           // V[r][p] = columns 2p, 2p+1 of row r
+            if constexpr (WT == Q4) {
+                // V[h][r][p] = columns 2p, 2p+1 of nibble half h (0: k + e, 1: k + 16 + e) of row r
+                unsigned V[2][4][4];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const bool ok = (R.rows_ok >> r) & 1u;
-                u4 w;
-                if (WT == Q4) w = deq8(R.cq[r], ok ? R.sc[r] : (_Float16)0.0f, (col0 & 31) >= 16);
-                else w = ok ? R.w[r] : u4{0u, 0u, 0u, 0u};
-                V[r][0] = w.x; V[r][1] = w.y; V[r][2] = w.z; V[r][3] = w.w;
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const _Float16 sr = ((R.rows_ok >> r) & 1u) ? R.sc[r] : (_Float16)0.0f;
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int p = cc >> 1;
-                const unsigned sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-                u4 out;
-                out.x = __builtin_amdgcn_perm(V[1][p], V[0][p], sel);
-                out.y = __builtin_amdgcn_perm(V[3][p], V[2][p], sel);
-                out.z = __builtin_amdgcn_perm(V[5][p], V[4][p], sel);
-                out.w = __builtin_amdgcn_perm(V[7][p], V[6][p], sel);
-                *reinterpret_cast<u4*>(s_wt + wt_off(8 * cg + cc, rg)) = out;
+                    for (int h = 0; h < 2; ++h) {
+                        const u4 w = deq8(R.cq[r], sr, h == 1);
+                        V[h][r][0] = w.x; V[h][r][1] = w.y; V[h][r][2] = w.z; V[h][r][3] = w.w;
+                    }
+                }
+                // each column's 4 rows (8 bytes) into its [column][k] row: k = 4 rg .. +3,
+                // the low or high half of 16-byte block rg / 2
+                const int lc0 = col0 - c0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) {
+                        const int p = cc >> 1;
+                        const unsigned sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                        const u2 out{__builtin_amdgcn_perm(V[h][1][p], V[h][0][p], sel),
+                                     __builtin_amdgcn_perm(V[h][3][p], V[h][2][p], sel)};
+                        *reinterpret_cast<u2*>(s_wt + wt_off(lc0 + 16 * h + cc, rg >> 1) + 8 * (rg & 1)) = out;
+                    }
+            } else {
+                unsigned V[8][4];                       // V[r][p] = columns 2p, 2p+1 of row r
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const bool ok = (R.rows_ok >> r) & 1u;
+                    const u4 w = ok ? R.w[r] : u4{0u, 0u, 0u, 0u};
+                    V[r][0] = w.x; V[r][1] = w.y; V[r][2] = w.z; V[r][3] = w.w;
+                }
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) {
+                    const int p = cc >> 1;
+                    const unsigned sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                    u4 out;
+                    out.x = __builtin_amdgcn_perm(V[1][p], V[0][p], sel);
+                    out.y = __builtin_amdgcn_perm(V[3][p], V[2][p], sel);
+                    out.z = __builtin_amdgcn_perm(V[5][p], V[4][p], sel);
+                    out.w = __builtin_amdgcn_perm(V[7][p], V[6][p], sel);
+                    *reinterpret_cast<u4*>(s_wt + wt_off(8 * cg + cc, rg)) = out;
+                }
             }
             if (act && R.full) {                        // (uniform) the usual step: no item to mask
 #pragma unroll
