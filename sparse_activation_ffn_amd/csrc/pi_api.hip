@@ -218,17 +218,17 @@ pi_status scratch_ptr(hipStream_t s, void** out) {
 }
 
 // ---- host side of the hybrid step --------------------------------------------------
-// One event per device (created on first use) marks the arrival of mask and x in
-// the host workspace; the host spins on it, then computes.
-std::mutex g_event_mu;
-hipEvent_t g_arrive[MAX_DEVICES] = {};
+// An event marks the arrival of mask and x in the host workspace; the host spins
+// on it, then computes.  One per host thread and device (created on first use,
+// kept until the process ends): calls from different threads, on different
+// streams, each wait for their own record.
+thread_local hipEvent_t g_arrive[MAX_DEVICES] = {};
 
 pi_status arrival_event(hipStream_t s, hipEvent_t* out) {
     int dev = -1;
     hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
     if (e != hipSuccess) return fail(PI_ERR_HIP, "stream device: %s", hipGetErrorString(e));
     if (dev < 0 || dev >= MAX_DEVICES) return fail(PI_ERR_HIP, "device %d out of range", dev);
-    std::lock_guard<std::mutex> lock(g_event_mu);
     if (!g_arrive[dev]) {
         int cur = -1;
         e = hipGetDevice(&cur);

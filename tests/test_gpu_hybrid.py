@@ -10,9 +10,9 @@ partition's sparse FFN over them in fp64.  Checked:
 - y_cold (the host partial) and y (merged) match the oracle to the layer tolerance
   (partials measured on the scale of the merged output);
 - y is close to the all-GPU split step (pi_sparse_ffn_split) on the same mask.
-Edge cases: no hot rows, no cold rows, B = 5, repeated calls on one host workspace;
-and the errors the call detects at run time (unpinned host workspace, cold weights
-in device memory).
+Edge cases: no hot rows, no cold rows, B = 5, repeated calls on one host workspace,
+two host threads calling at once on two streams; and the errors the call detects
+at run time (unpinned host workspace, cold weights in device memory).
 """
 import numpy as np
 import pytest
@@ -142,8 +142,8 @@ def test_hybrid_runtime_errors():
 
 def test_hybrid_full_size_opt30b_shape():
     """OPT-30B-shaped layer (d 7168, n 28672) with the profiled neuron index and a 26 %
-    hot partition on the GPU, the rest in host memory, batch 1: sampled output
-    columns against the oracle's full-size result over the step's lists."""
+    hot partition on the GPU, the rest in host memory, batch 1: the output against
+    the oracle's full-size result over the step's lists."""
     wl = S.WORKLOADS["opt30b-fp16"]
     L = S.make_layer(wl)
     base = DeviceLayer.upload(L, DEV)
@@ -174,3 +174,46 @@ def test_hybrid_full_size_opt30b_shape():
     y_o = O.merge(O.sparse_ffn(O.Part.from_layer(Lh, 0, n_hot), x_np, hot_o),
                   O.sparse_ffn(O.Part.from_layer(Lh, n_hot, wl.n), x_np, cold_o))
     check_close(_np(buf.y), y_o, "f16")
+
+
+def test_hybrid_calls_from_two_threads_on_two_streams():
+    """Two host threads, each with its own buffers and stream, run hybrid steps at the
+    same time; each waits for its own mask and x (the arrival event is per thread) and
+    gets its own step's result."""
+    import threading
+    st = [Setup("f16", 1), Setup("f16", 1)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    out = [None, None]
+    errs = []
+
+    def run(k):
+        try:
+            s = st[k]
+            res = []
+            with torch.cuda.stream(streams[k]):
+                for step in range(4):
+                    x_np = S.make_x(s.wl, 0, 10 * k + step, 1)
+                    x = torch.from_numpy(x_np).to(DEV)
+                    b = s.buf
+                    pb.pi_predict(s.dl.predictor(), x, b.mask, None, None, b.ws, stream=streams[k])
+                    pb.pi_sparse_ffn_hybrid(s.hot, s.cold, x, b.mask, b.lists, s.y_cold, b.y, b.ws,
+                                            s.host_ws, 0, stream=streams[k])
+                    streams[k].synchronize()
+                    res.append((x_np, _np(b.mask).view(np.uint64).copy(), _np(b.y).copy()))
+            out[k] = res
+        except Exception as e:  # noqa: BLE001
+            errs.append(e)
+
+    th = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs, errs
+    for k in range(2):
+        s = st[k]
+        for x_np, mask, y in out[k]:
+            hot_o, cold_o = O.compact(mask, s.wl.n, s.n_hot)
+            y_o = O.merge(O.sparse_ffn(O.Part.from_layer(s.L, 0, s.n_hot), x_np, hot_o),
+                          O.sparse_ffn(O.Part.from_layer(s.L, s.n_hot, s.wl.n), x_np, cold_o))
+            check_close(y, y_o, s.wl.wdtype)
