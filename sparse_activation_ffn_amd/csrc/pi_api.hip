@@ -663,11 +663,13 @@ pi_status predict_launch(const pi_predictor* p, const void* x, int B, int xdtype
         auto pred1 = mt == 1 ? k_mfma_pred1<1> : mt == 2 ? k_mfma_pred1<2> : k_mfma_pred1<4>;
         TRY(launch(PI_K_PRED_L1, pred1, g1, dim3(MFMA_WG), 0, s, (const uint8_t*)p->P1t,
                    (const uint8_t*)x, p->d, p->r, B, part));
+        // the u region holds the second layer's f16 operand: uh [B][r] then ul [B][r]
+        _Float16* uhl = reinterpret_cast<_Float16*>(u);
         TRY(launch(PI_K_PRED_L1, k_u_relu, dim3(B), dim3(THREADS), 0, s, (const float*)part, B, p->r,
-                   u, uscale));
+                   uhl, uscale));
         auto pred2 = mt == 1 ? k_mfma_pred2<1> : mt == 2 ? k_mfma_pred2<2> : k_mfma_pred2<4>;
         TRY(launch(PI_K_PRED_L2, pred2, dim3((p->n + P2_ROWS - 1) / P2_ROWS), dim3(MFMA_WG), 0, s,
-                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const float*)u, (const float*)uscale,
+                   (const uint8_t*)p->P2t, p->b2, p->threshold, (const _Float16*)uhl, (const float*)uscale,
                    p->n, p->r, B, mask, logits));
     } else {
         pi_status st;

@@ -893,21 +893,25 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred1(const uint8_t* __restric
 
 // u = ReLU(sum of the P1_KS slice partials, in slice order), one workgroup per
 // token (r <= 4096: at most 16 values per thread).  The workgroup also finds the
-// token's largest u and writes the power of two uscale[b] = 2^(14 - e), e =
-// floor(log2(max u)), that maps that maximum into [2^14, 2^15): the second
-// layer splits u * uscale into two f16 parts, and the power of two keeps the
-// high part finite and normal whatever the magnitude of u (u itself is stored
-// unscaled, fp32).
+// token's largest u and the power of two uscale[b] = 2^(14 - e), e =
+// floor(log2(max u)), that maps that maximum into [2^14, 2^15), and writes the
+// second layer's operand once for every workgroup of that layer: u * uscale
+// split into two f16 parts, uh = f16(u s) and ul = f16(u s - uh) ([B][r] each,
+// uh then ul).  The power of two keeps the high part finite and normal whatever
+// the magnitude of u.
 constexpr int UR_MAX = 16;      // u values per thread of k_u_relu (r <= 16 * 256)
 __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ part, int B, int r,
-                                                    float* __restrict__ u, float* __restrict__ uscale) {
+                                                    _Float16* __restrict__ uhl, float* __restrict__ uscale) {
     __shared__ float s_max[NWAVES];
+    __shared__ float s_scale;
     const int b = blockIdx.x;
     const int64_t len = (int64_t)B * r;
     float vmax = 0.0f;
+    float uv[UR_MAX];
 #pragma unroll
     for (int t = 0; t < UR_MAX; ++t) {
         const int j = threadIdx.x + THREADS * t;
+        uv[t] = 0.0f;
         if (j < r) {
             const int64_t at = (int64_t)b * r + j;
             float v[P1_KS];
@@ -916,9 +920,8 @@ __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ pa
             float sum = v[0];
 #pragma unroll
             for (int k = 1; k < P1_KS; ++k) sum += v[k];
-            const float uv = sum > 0.0f ? sum : 0.0f;
-            u[at] = uv;
-            vmax = fmaxf(vmax, uv);
+            uv[t] = sum > 0.0f ? sum : 0.0f;
+            vmax = fmaxf(vmax, uv[t]);
         }
     }
     // largest u of the token (max is exact, so the order does not matter)
@@ -932,7 +935,22 @@ __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ pa
         for (int w = 1; w < NWAVES; ++w) m = fmaxf(m, s_max[w]);
         // m == 0 (every u zero) or not finite: no scaling
         const int e = (m > 0.0f && m <= 3.0e38f) ? ilogbf(m) : 14;
-        uscale[b] = ldexpf(1.0f, 14 - e);
+        const float sc = ldexpf(1.0f, 14 - e);
+        uscale[b] = sc;
+        s_scale = sc;
+    }
+    __syncthreads();
+    const float sc = s_scale;
+#pragma unroll
+    for (int t = 0; t < UR_MAX; ++t) {
+        const int j = threadIdx.x + THREADS * t;
+        if (j < r) {
+            const int64_t at = (int64_t)b * r + j;
+            const float a = uv[t] * sc;
+            const _Float16 hi = (_Float16)a;
+            uhl[at] = hi;
+            uhl[len + at] = (_Float16)(a - (float)hi);
+        }
     }
 }
 
@@ -951,14 +969,15 @@ __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ pa
 constexpr int P2_ROWS = 128;    // neurons per workgroup (32 per wave)
 
 template <int MT>
-__global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restrict__ P2t,
+__global__ __launch_bounds__(MFMA_WG) __attribute__((amdgpu_waves_per_eu(2))) void k_mfma_pred2(
+                                                       const uint8_t* __restrict__ P2t,
                                                        const float* __restrict__ b2, float thr,
-                                                       const float* __restrict__ u,
+                                                       const _Float16* __restrict__ uhl,
                                                        const float* __restrict__ uscale, int n, int r,
                                                        int B, uint64_t* __restrict__ mask,
                                                        float* __restrict__ logits) {
     constexpr int J = P2_ROWS * 16 / MFMA_WG;         // 16-byte weight loads per thread
-    constexpr int UN = 16 * MT * 16;                  // 8-float pieces of the u slice
+    constexpr int UN = 16 * MT * 16;                  // 8-element pieces of the u slice
     constexpr int UJ = (UN + MFMA_WG - 1) / MFMA_WG;  // per thread
     constexpr int D = 2;
     __shared__ __attribute__((aligned(16))) uint8_t s_uh[16 * MT * 256];
@@ -979,8 +998,9 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
     }
     struct Stage {
         u4 w[J];
-        f4 uv[UJ][2];
+        u4 uh[UJ], ul[UJ];
     };
+    const int64_t ulen = (int64_t)B * r;
     auto load = [&](Stage& R, int s) {
         const int k0 = s * KS;
 #pragma unroll
@@ -988,15 +1008,11 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
 #pragma unroll
         for (int j = 0; j < UJ; ++j) {
             const int t = min(tid + MFMA_WG * j, UN - 1), m = t >> 4, kb = t & 15;
-            const f4* up = reinterpret_cast<const f4*>(u + (int64_t)min(m, B - 1) * r + k0 + 8 * kb);
-            R.uv[j][0] = up[0];
-            R.uv[j][1] = up[1];
+            const int64_t at = (int64_t)min(m, B - 1) * r + k0 + 8 * kb;
+            R.uh[j] = ld16(uhl + at);
+            R.ul[j] = ld16(uhl + ulen + at);
         }
     };
-    // per-token scales of this thread's u pieces (fixed for the whole kernel)
-    float usc[UJ];
-#pragma unroll
-    for (int j = 0; j < UJ; ++j) usc[j] = uscale[min((min(tid + MFMA_WG * j, UN - 1) >> 4), B - 1)];
     auto store = [&](const Stage& R, bool act) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -1008,19 +1024,8 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_pred2(const uint8_t* __restric
             const int t = tid + MFMA_WG * j, m = t >> 4, kb = t & 15;
             if (t < UN) {
                 const bool ok = act && m < B;
-                const float v[8] = {R.uv[j][0].x, R.uv[j][0].y, R.uv[j][0].z, R.uv[j][0].w,
-                                    R.uv[j][1].x, R.uv[j][1].y, R.uv[j][1].z, R.uv[j][1].w};
-                unsigned hw[4], lw[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float a0 = ok ? v[2 * p] * usc[j] : 0.0f, a1 = ok ? v[2 * p + 1] * usc[j] : 0.0f;
-                    const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
-                    const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
-                    hw[p] = (unsigned)__builtin_bit_cast(uint16_t, h0) | ((unsigned)__builtin_bit_cast(uint16_t, h1) << 16);
-                    lw[p] = (unsigned)__builtin_bit_cast(uint16_t, l0) | ((unsigned)__builtin_bit_cast(uint16_t, l1) << 16);
-                }
-                *reinterpret_cast<u4*>(s_uh + swz(m, kb)) = u4{hw[0], hw[1], hw[2], hw[3]};
-                *reinterpret_cast<u4*>(s_ul + swz(m, kb)) = u4{lw[0], lw[1], lw[2], lw[3]};
+                *reinterpret_cast<u4*>(s_uh + swz(m, kb)) = ok ? R.uh[j] : u4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u4*>(s_ul + swz(m, kb)) = ok ? R.ul[j] : u4{0u, 0u, 0u, 0u};
             }
         }
     };
