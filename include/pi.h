@@ -371,16 +371,19 @@ size_t pi_hybrid_host_bytes(int32_t d, int32_t n, int32_t B);
  *          pi_hybrid_host_bytes(d, n, B) bytes;
  *   threads host threads for the cold rows (0 = all of the pool);
  *   info   [host] optional record of the call.
- * Order of work: mask and x are copied to host_ws on `stream`, the hot FFN is
- * enqueued behind them, the host waits for the copies only, computes the cold
- * rows (pi_host_sparse_ffn) while the GPU runs the hot ones, then enqueues
- * the copy of its partial to y_cold and the merge.  Unlike the other calls
- * this one blocks the host until the copies of mask and x are done and the
- * host part is computed; it returns with the copy and the merge enqueued.
- * The host workspace must not be reused from another stream or thread until
- * this stream has passed the merge.  Not capturable in a HIP graph.  Errors
- * are detected before anything is enqueued (host_ws not pinned and cold
- * weights in device memory included: PI_ERR_ARG).
+ * Order of work: a kernel on `stream` writes mask and x into host_ws (pinned
+ * memory is mapped for the GPU), the hot FFN is enqueued behind it, the host
+ * waits for that kernel only, computes the cold rows (pi_host_sparse_ffn)
+ * while the GPU runs the hot ones into y, then enqueues the merge kernel, which
+ * reads the host's partial from host_ws into y_cold and adds it to y.  Unlike
+ * the other calls this one blocks the host until mask and x have arrived and
+ * the host part is computed; it returns with the merge enqueued.  The host
+ * workspace must not be reused from another stream or thread until this
+ * stream has passed the merge; calls from different host threads on different
+ * streams (each with its own buffers) may run at the same time, their host
+ * parts one after the other.  Not capturable in a HIP graph.  Errors are
+ * detected before anything is enqueued (host_ws not pinned and cold weights
+ * in device memory included: PI_ERR_ARG).
  */
 pi_status pi_sparse_ffn_hybrid(const pi_ffn_part* hot, const pi_ffn_part* cold, const void* x,
                                int32_t B, int32_t xdtype, const uint64_t* mask,
