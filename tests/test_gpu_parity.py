@@ -447,7 +447,7 @@ def test_compact_ignores_tail_bits():
 
 def test_opt30b_full_with_index():
     """OPT-30B-shaped layer (d 7168, n 28672, rank 1024, fp16), 26% hot partition from
-    1024 profiling samples, split + merge, eight decode steps."""
+    1024 profiling samples, split + merge, all 64 decode steps of the workload."""
     wl = S.WORKLOADS["opt30b-fp16"]
     L = S.make_layer(wl)
     dl = DeviceLayer.upload(L, DEV)
@@ -455,23 +455,27 @@ def test_opt30b_full_with_index():
     Lh, n_hot = index_layer(L, dl, wl.profile_samples, rows_checked=rows)
     assert n_hot == 7454
     buf = StepBuffers(dl, 1, DEV)
-    for step in range(8):
+    for step in range(wl.steps):
         x = S.make_x(wl, 0, step, 1)
         e, namb, na = check_step(Lh, n_hot, x, run_step(dl, buf, x))
-        log(f"  opt30b step {step}: active {na} (hot {int(buf.counts[0])}), ambiguous {namb}, "
-            f"err {e:.2e}")
+        if step % 8 == 0 or step == wl.steps - 1:
+            log(f"  opt30b step {step}: active {na} (hot {int(buf.counts[0])}), ambiguous {namb}, "
+                f"err {e:.2e}")
 
 
-@pytest.mark.parametrize("B", [1, 4])
-def test_reglu70b_full(B):
+@pytest.mark.parametrize("B,steps", [(1, 64), (4, 24)])
+def test_reglu70b_full(B, steps):
+    """LLaMA(ReGLU)-70B-shaped layer (d 8192, n 28672, fp16) at batch 1 (the fused
+    kernel) and 4 (the matrix-core path): the first `steps` decode steps."""
     wl = S.WORKLOADS["llama70b-reglu-fp16"]
     L = S.make_layer(wl)
     dl = DeviceLayer.upload(L, DEV)
     buf = StepBuffers(dl, B, DEV)
-    for step in range(2):
+    for step in range(steps):
         x = S.make_x(wl, 0, step, B)
         e, namb, na = check_step(L, wl.n, x, run_step(dl, buf, x))
-        log(f"  reglu70b B={B} step {step}: union active {na}, ambiguous {namb}, err {e:.2e}")
+        if step % 8 == 0 or step == steps - 1:
+            log(f"  reglu70b B={B} step {step}: union active {na}, ambiguous {namb}, err {e:.2e}")
 
 
 @pytest.mark.parametrize("layer", [0, 29, 59])
@@ -525,20 +529,22 @@ def test_falcon40b_device_drawn_layer():
     log(f"  device-drawn falcon layer {li}: 16 steps, last active {na}, worst err {worst:.2e}")
 
 
-@pytest.mark.parametrize("B", [1, 8, 64])
-def test_opt175b_q4_full(B):
-    """OPT-175B-shaped Q4_0 layer: the union mask of all B tokens against the oracle's
-    predictor (ambiguity band), the list bit-exact, the FFN on up to four tokens over
-    the GPU's union list."""
+@pytest.mark.parametrize("B,steps", [(1, 64), (8, 16), (64, 6)])
+def test_opt175b_q4_full(B, steps):
+    """OPT-175B-shaped Q4_0 layer, the first `steps` decode steps: the union mask of
+    all B tokens against the oracle's predictor (ambiguity band), the list bit-exact,
+    the FFN on up to four tokens over the GPU's union list."""
     wl = S.WORKLOADS["opt175b-q4_0"]
     L = S.make_layer(wl)
     dl = DeviceLayer.upload(L, DEV)
     buf = StepBuffers(dl, B, DEV)
-    x = S.make_x(wl, 0, 0, B)
-    out = run_step(dl, buf, x)
     tokens = None if B == 1 else sorted({0, B // 3, (2 * B) // 3, B - 1})
-    e, namb, na = check_step(L, wl.n, x, out, tokens=tokens)
-    log(f"  q4_0 B={B}: union active {na}, ambiguous {namb}, err {e:.2e}")
+    for step in range(steps):
+        x = S.make_x(wl, 0, step, B)
+        out = run_step(dl, buf, x)
+        e, namb, na = check_step(L, wl.n, x, out, tokens=tokens)
+        if step % 8 == 0 or step == steps - 1:
+            log(f"  q4_0 B={B} step {step}: union active {na}, ambiguous {namb}, err {e:.2e}")
 
 
 def test_bandwidth_aware_split_with_cold_rows_in_host_memory():
