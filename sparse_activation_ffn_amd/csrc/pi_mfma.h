@@ -908,20 +908,29 @@ __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ pa
     const int64_t len = (int64_t)B * r;
     float vmax = 0.0f;
     float uv[UR_MAX];
+    // four values at a time, their 4 x P1_KS loads issued together (clamped
+    // addresses, unconditional) before any of them is summed
+    constexpr int UG = 4;
 #pragma unroll
-    for (int t = 0; t < UR_MAX; ++t) {
-        const int j = threadIdx.x + THREADS * t;
-        uv[t] = 0.0f;
-        if (j < r) {
+    for (int t0 = 0; t0 < UR_MAX; t0 += UG) {
+        if (threadIdx.x + THREADS * t0 >= r) break;       // this thread has no values left
+        float v[UG][P1_KS];
+#pragma unroll
+        for (int g = 0; g < UG; ++g) {
+            const int j = min(threadIdx.x + THREADS * (t0 + g), r - 1);
             const int64_t at = (int64_t)b * r + j;
-            float v[P1_KS];
 #pragma unroll
-            for (int k = 0; k < P1_KS; ++k) v[k] = part[k * len + at];
-            float sum = v[0];
+            for (int k = 0; k < P1_KS; ++k) v[g][k] = part[k * len + at];
+        }
 #pragma unroll
-            for (int k = 1; k < P1_KS; ++k) sum += v[k];
-            uv[t] = sum > 0.0f ? sum : 0.0f;
-            vmax = fmaxf(vmax, uv[t]);
+        for (int g = 0; g < UG; ++g) {
+            const int j = threadIdx.x + THREADS * (t0 + g);
+            float sum = v[g][0];
+#pragma unroll
+            for (int k = 1; k < P1_KS; ++k) sum += v[g][k];
+            const float u1 = (j < r && sum > 0.0f) ? sum : 0.0f;
+            uv[t0 + g] = u1;
+            vmax = fmaxf(vmax, u1);
         }
     }
     // largest u of the token (max is exact, so the order does not matter)
@@ -944,13 +953,12 @@ __global__ __launch_bounds__(THREADS) void k_u_relu(const float* __restrict__ pa
 #pragma unroll
     for (int t = 0; t < UR_MAX; ++t) {
         const int j = threadIdx.x + THREADS * t;
-        if (j < r) {
-            const int64_t at = (int64_t)b * r + j;
-            const float a = uv[t] * sc;
-            const _Float16 hi = (_Float16)a;
-            uhl[at] = hi;
-            uhl[len + at] = (_Float16)(a - (float)hi);
-        }
+        if (j >= r) break;
+        const int64_t at = (int64_t)b * r + j;
+        const float a = uv[t] * sc;
+        const _Float16 hi = (_Float16)a;
+        uhl[at] = hi;
+        uhl[len + at] = (_Float16)(a - (float)hi);
     }
 }
 
