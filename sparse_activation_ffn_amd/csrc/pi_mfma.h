@@ -307,16 +307,31 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
     return true;
 }
 
+// The part of an up tile (16 MT tokens x 64 NT items) one wave computes.  With 64
+// tokens and 64 items the four waves take 2 x 2 quarters (32 tokens x 32 items
+// each), so a wave reads 2 + 2 operand fragments per K slice instead of 4 + 1;
+// otherwise each wave takes all tokens and 16 NT items.
+template <int MT, int NT> struct WaveTile {
+    static constexpr bool QUAD = MT == 4 && NT == 1;
+    static constexpr int MW = QUAD ? 2 : MT;          // token tiles of 16 per wave
+    static constexpr int NW = QUAD ? 2 : NT;          // item tiles of 16 per wave
+    __device__ static int tok0(int wv) { return QUAD ? 32 * (wv & 1) : 0; }
+    __device__ static int item0(int wv) { return QUAD ? 32 * (wv >> 1) : 16 * NT * wv; }
+};
+
 // Bias, activation and the f16 h write of an up tile: lane holds
-// acc[g][jn][mt][i] = D[token 16 mt + 4 q + i][item 16 NT wv + 16 jn + c].
+// acc[g][jn][mt][i] = D[token tok0 + 16 mt + 4 q + i][item item0 + 16 jn + c].
 template <int ACT, int NM, int NT, int MT>
-__device__ __forceinline__ void up_epilogue(const FfnArgs& a, const f4m (&acc)[NM][NT][MT], const int* s_row,
-                                            const int* s_part, int i0, int H, int T, _Float16* __restrict__ h16) {
+__device__ __forceinline__ void up_epilogue(const FfnArgs& a,
+                                            const f4m (&acc)[NM][WaveTile<MT, NT>::NW][WaveTile<MT, NT>::MW],
+                                            const int* s_row, const int* s_part, int i0, int H, int T,
+                                            _Float16* __restrict__ h16) {
+    using WT_ = WaveTile<MT, NT>;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int jn = 0; jn < NT; ++jn) {
-        const int r = 16 * NT * wv + 16 * jn + c;
+    for (int jn = 0; jn < WT_::NW; ++jn) {
+        const int r = WT_::item0(wv) + 16 * jn + c;
         const int row = s_row[r], part = s_part[r];
         const int item = i0 + r;
         if (item < T) {
@@ -324,10 +339,10 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const f4m (&acc)[N
             const float bu = (row >= 0 && a.bup[part]) ? a.bup[part][row] : 0.0f;
             const float bg = (ACT == REGLU && row >= 0 && a.bgate[part]) ? a.bgate[part][row] : 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < WT_::MW; ++mt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int tok = 16 * mt + 4 * q + i;
+                    const int tok = WT_::tok0(wv) + 16 * mt + 4 * q + i;
                     if (tok < a.B) {
                         const float up = acc[0][jn][mt][i] + bu;
                         float hv;
@@ -352,13 +367,15 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const f4m (&acc)[N
 // Split over K: this slice's fp32 pre-activations of the tile (slice 0 adds
 // the biases), for k_up_finish.  Same lane mapping as up_epilogue.
 template <int NM, int NT, int MT>
-__device__ __forceinline__ void up_partials(const FfnArgs& a, const f4m (&acc)[NM][NT][MT], const int* s_row,
-                                            const int* s_part, int i0, int T, int slice) {
+__device__ __forceinline__ void up_partials(const FfnArgs& a,
+                                            const f4m (&acc)[NM][WaveTile<MT, NT>::NW][WaveTile<MT, NT>::MW],
+                                            const int* s_row, const int* s_part, int i0, int T, int slice) {
+    using WT_ = WaveTile<MT, NT>;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int jn = 0; jn < NT; ++jn) {
-        const int r = 16 * NT * wv + 16 * jn + c;
+    for (int jn = 0; jn < WT_::NW; ++jn) {
+        const int r = WT_::item0(wv) + 16 * jn + c;
         const int row = s_row[r], part = s_part[r];
         const int item = i0 + r;
         if (item < T) {
@@ -368,10 +385,10 @@ __device__ __forceinline__ void up_partials(const FfnArgs& a, const f4m (&acc)[N
 #pragma unroll
             for (int g = 0; g < NM; ++g)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < WT_::MW; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int tok = 16 * mt + 4 * q + i;
+                        const int tok = WT_::tok0(wv) + 16 * mt + 4 * q + i;
                         if (tok < a.B)
                             a.upart[((int64_t)(slice * NM + g) * a.B + tok) * a.upart_ld + item] =
                                 acc[g][jn][mt][i] + bias[g];
@@ -503,42 +520,46 @@ __global__ __launch_bounds__(MFMA_WG) void k_mfma_up(FfnArgs a, _Float16* __rest
             if (t < XN) *reinterpret_cast<u4*>(s_x + swz(m, kb)) = act ? R.xv[j] : u4{0u, 0u, 0u, 0u};
         }
     };
-    f4m acc[NM][NT][MT];
+    using WTL = WaveTile<MT, NT>;
+    constexpr int MW = WTL::MW, NW = WTL::NW;
+    const int tok0 = WTL::tok0(wv), item0 = WTL::item0(wv);
+    f4m acc[NM][NW][MW];
 #pragma unroll
     for (int g = 0; g < NM; ++g)
 #pragma unroll
-        for (int jn = 0; jn < NT; ++jn)
+        for (int jn = 0; jn < NW; ++jn)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[g][jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < MW; ++mt) acc[g][jn][mt] = f4m{0.f, 0.f, 0.f, 0.f};
     // every fragment of the step is read before the first product: the LDS
     // latency is paid once per step, not once per 32-wide K slice
     auto compute = [&]() {
         constexpr int NKS = KS / 32;
-        h8 ax[NKS][MT], bw[NKS][NM][NT];
+        h8 ax[NKS][MW], bw[NKS][NM][NW];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int kb = 4 * ks + q;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) ax[ks][mt] = *reinterpret_cast<const h8*>(s_x + swz(16 * mt + c, kb));
+            for (int mt = 0; mt < MW; ++mt)
+                ax[ks][mt] = *reinterpret_cast<const h8*>(s_x + swz(tok0 + 16 * mt + c, kb));
 #pragma unroll
             for (int g = 0; g < NM; ++g)
 #pragma unroll
-                for (int jn = 0; jn < NT; ++jn)
-                    bw[ks][g][jn] = *reinterpret_cast<const h8*>(s_w[g] + swz(16 * NT * wv + 16 * jn + c, kb));
+                for (int jn = 0; jn < NW; ++jn)
+                    bw[ks][g][jn] = *reinterpret_cast<const h8*>(s_w[g] + swz(item0 + 16 * jn + c, kb));
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int g = 0; g < NM; ++g)
 #pragma unroll
-                for (int jn = 0; jn < NT; ++jn)
+                for (int jn = 0; jn < NW; ++jn)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+                    for (int mt = 0; mt < MW; ++mt)
                         acc[g][jn][mt] = mfma32(ax[ks][mt], bw[ks][g][jn], acc[g][jn][mt]);
         // keep the order: the compiler's scheduler would interleave each product
         // with its own fragment reads again
-        __builtin_amdgcn_sched_group_barrier(0x100, NKS * (MT + NM * NT), 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, NKS * NM * NT * MT, 0);     // matrix-core ops
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS * (MW + NM * NW), 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, NKS * NM * NW * MW, 0);     // matrix-core ops
     };
     const int steps = a.d / KS;
     run_pipeline<D, Stage>(steps * slice / nsl, steps * (slice + 1) / nsl, load, store, compute);
