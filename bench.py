@@ -238,15 +238,23 @@ def cpu_baseline(wl, L, n_hot, B, budget_s=8.0):
         return el / steps * 1e6, steps
 
     try:
-        one_us, one_n = leg(1)
+        log(f"[bench] oracle on {threads} threads ...")
         all_us, all_n = leg(threads)
+        # one single-threaded step costs about threads times the threaded one: skipped
+        # where that alone would exceed a minute (the large batches)
+        one_us = one_n = None
+        if all_us * threads * 1e-6 <= 60.0:
+            log("[bench] oracle on 1 thread ...")
+            one_us, one_n = leg(1)
     finally:
         O.set_threads(1)
+    one = (f"single-threaded: {one_n} steps" if one_n is not None
+           else "single-threaded leg skipped (one step would take over a minute)")
     return {"value": round(all_us, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
             "sample": f"{all_n} layer steps of the same {wl.name} layer (batch {B}), C oracle "
-                      f"(fp64 accumulation) with its outer loops on {threads} threads; "
-                      f"single-threaded: {one_n} steps",
-            "single_thread_us": round(one_us, 1), "nproc": nproc, "cpu_model": model}
+                      f"(fp64 accumulation) with its outer loops on {threads} threads; {one}",
+            "single_thread_us": None if one_us is None else round(one_us, 1), "nproc": nproc,
+            "cpu_model": model}
 
 
 def time_stream(pb, torch, nbytes, dev, launches=16, host=False):
