@@ -142,6 +142,7 @@ size_t ws_h_bytes(int n, int B) {
 // (ReGLU-70B-shaped layer 132 -> 139 us), so those run unsplit.
 constexpr int UP_SPLIT_SMALL_B = 4;
 constexpr int UP_SPLIT_MAX_B = 16;
+static_assert(UP_SPLIT_SMALL_B <= UP_FINISH_MAX_S, "k_up_finish holds at most UP_FINISH_MAX_S slices");
 int up_split_want(int B, int wt) { return wt == Q4 && B <= UP_SPLIT_MAX_B ? UP_SPLIT_SMALL_B : 1; }
 int64_t up_part_ld(int n) { return (int64_t)(n + 63) / 64 * 64; }
 
@@ -491,7 +492,7 @@ pi_status launch_mfma_up(const FfnArgs& a, int rows_cap, hipStream_t s) {
     if (a.ksplit <= 1) return PI_OK;
     // the slices' sum and the activation (item count from the device)
     constexpr int NM = ACT == REGLU ? 2 : 1;
-    const int gx = std::max(1, std::min((rows_cap + THREADS - 1) / THREADS, 64));
+    const int gx = std::max(1, (rows_cap + THREADS - 1) / THREADS);   // one item per thread
     return launch(PI_K_UP_FINISH, k_up_finish<ACT, NM>, dim3(gx, a.B), dim3(THREADS), 0, s,
                   (const float*)a.upart, a.ksplit, a.upart_ld, a.B, (const int*)a.up_ht,
                   reinterpret_cast<_Float16*>(a.h), a.h_ld);

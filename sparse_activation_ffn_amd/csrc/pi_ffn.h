@@ -448,6 +448,19 @@ constexpr int RS = 16;                // partial slices per element
 __global__ __launch_bounds__(RE * RS) void k_reduce_parts(FfnArgs a, DownOut o) {
     __shared__ float s_h[RS][RE], s_c[RS][RE];
     const int e = threadIdx.x % RE, s = threadIdx.x / RE;
+    const int64_t len = (int64_t)a.B * a.d;
+    const int64_t at = (int64_t)blockIdx.x * RE + e;
+    const int64_t atc = at < len ? at : len - 1;
+    constexpr int R = 16;              // partials in flight per thread (256 partials per pass)
+    // the first pass's partials are loaded before the hot / cold counts: their
+    // addresses do not depend on the counts, which take a chain of dependent
+    // scalar loads and a division to turn into the hot workgroup count
+    float v[R];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) v[q] = o.partials[min(k0 + RS * q, o.nch - 1) * len + atc];
+    };
+    load(s);
     int H, C;
     if (a.mask) {                      // counts were written by the fused kernel
         H = a.out_counts[0];
@@ -457,21 +470,17 @@ __global__ __launch_bounds__(RE * RS) void k_reduce_parts(FfnArgs a, DownOut o) 
     }
     int part, lo, hi, nh;
     chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
-    const int64_t len = (int64_t)a.B * a.d;
-    const int64_t at = (int64_t)blockIdx.x * RE + e;
-    const int64_t atc = at < len ? at : len - 1;
-    constexpr int R = 16;              // partials in flight per thread (256 partials per pass)
     float yh = 0.0f, yc = 0.0f;
-    for (int k0 = s; k0 < o.nch; k0 += RS * R) {
-        float v[R];
-#pragma unroll
-        for (int q = 0; q < R; ++q) v[q] = o.partials[min(k0 + RS * q, o.nch - 1) * len + atc];
+    for (int k0 = s;;) {
 #pragma unroll
         for (int q = 0; q < R; ++q) {
             const int kk = k0 + RS * q;
             if (kk < nh) yh += v[q];
             else if (kk < o.nch) yc += v[q];
         }
+        k0 += RS * R;
+        if (k0 >= o.nch) break;
+        load(k0);
     }
     s_h[s][e] = yh;
     s_c[s][e] = yc;

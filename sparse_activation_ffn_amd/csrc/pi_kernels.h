@@ -666,21 +666,28 @@ __global__ __launch_bounds__(THREADS) void k_down(FfnArgs a, DownOut o) {
 // hot chunks in order give y_hot, the cold chunks in order give y_cold, and
 // y = y_hot + y_cold is the merge.  Deterministic (fixed order, no atomics).
 __global__ __launch_bounds__(THREADS) void k_reduce(FfnArgs a, DownOut o) {
-    int H, C;
-    item_counts(a, H, C);
-    int part, lo, hi, nh;
-    chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
     const int64_t len = (int64_t)a.B * a.d;           // a multiple of 4 (d % 64 == 0)
     const int64_t len4 = len / 4;
     const int64_t stride = (int64_t)gridDim.x * THREADS;
     const f4* P = reinterpret_cast<const f4*>(o.partials);
     constexpr int R = 8;       // partial loads in flight per thread (branch-free batches)
-    for (int64_t at = (int64_t)blockIdx.x * THREADS + threadIdx.x; at < len4; at += stride) {
-        f4 yh = {0.f, 0.f, 0.f, 0.f}, yc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < o.nch; k0 += R) {
-            f4 v[R];
+    f4 v[R];
+    auto load = [&](int64_t at, int k0) {
+        const int64_t ac = at < len4 ? at : len4 - 1;
 #pragma unroll
-            for (int q = 0; q < R; ++q) v[q] = P[min(k0 + q, o.nch - 1) * len4 + at];
+        for (int q = 0; q < R; ++q) v[q] = P[min(k0 + q, o.nch - 1) * len4 + ac];
+    };
+    // the first partials are loaded before the item counts, which they do not
+    // depend on (the counts take dependent loads and a division)
+    const int64_t at0 = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+    load(at0, 0);
+    int H, C;
+    item_counts(a, H, C);
+    int part, lo, hi, nh;
+    chunk_range(o.nch, H, C, 0, part, lo, hi, nh);
+    for (int64_t at = at0; at < len4; at += stride) {
+        f4 yh = {0.f, 0.f, 0.f, 0.f}, yc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0;;) {
 #pragma unroll
             for (int q = 0; q < R; ++q) {
                 const int kk = k0 + q;
@@ -690,7 +697,11 @@ __global__ __launch_bounds__(THREADS) void k_reduce(FfnArgs a, DownOut o) {
                     yc.x += v[q].x; yc.y += v[q].y; yc.z += v[q].z; yc.w += v[q].w;
                 }
             }
+            k0 += R;
+            if (k0 >= o.nch) break;
+            load(at, k0);
         }
+        if (at + stride < len4) load(at + stride, 0);
         if (o.y_part[0]) reinterpret_cast<f4*>(o.y_part[0])[at] = yh;
         if (o.y_part[1]) reinterpret_cast<f4*>(o.y_part[1])[at] = yc;
         if (o.y) reinterpret_cast<f4*>(o.y)[at] = f4{yh.x + yc.x, yh.y + yc.y, yh.z + yc.z, yh.w + yc.w};

@@ -398,20 +398,38 @@ __device__ __forceinline__ void up_partials(const FfnArgs& a,
 }
 
 // The slices' sum, the activation and the f16 h write of every (token, item)
-// of the step (fixed slice order).  grid (x: item blocks, y: tokens).
+// of the step (fixed slice order).  grid (x: item blocks, y: tokens).  A
+// thread's first slice values are loaded before the item count, whose load
+// they do not depend on (items below ld are inside the slices' buffer).
+constexpr int UP_FINISH_MAX_S = 4;    // most K slices the split up kernel writes
 template <int ACT, int NM>
 __global__ __launch_bounds__(THREADS) void k_up_finish(const float* __restrict__ upart, int S, int ld, int B,
                                                        const int* __restrict__ ht, _Float16* __restrict__ h16,
                                                        int h_ld) {
-    const int H = ht[0], T = ht[1];
     const int tok = blockIdx.y;
-    for (int item = blockIdx.x * THREADS + threadIdx.x; item < T; item += gridDim.x * THREADS) {
+    const int stride = gridDim.x * THREADS;
+    const int item0 = blockIdx.x * THREADS + threadIdx.x;
+    float p[UP_FINISH_MAX_S][NM];
+    auto load = [&](int item) {
+        const int64_t ic = min(item, ld - 1);
+#pragma unroll
+        for (int k = 0; k < UP_FINISH_MAX_S; ++k)
+            if (k < S)
+#pragma unroll
+                for (int g = 0; g < NM; ++g) p[k][g] = upart[((int64_t)(k * NM + g) * B + tok) * ld + ic];
+    };
+    load(item0);
+    const int H = ht[0], T = ht[1];
+    for (int item = item0; item < T; item += stride) {
         float v[NM];
 #pragma unroll
         for (int g = 0; g < NM; ++g) v[g] = 0.0f;
-        for (int k = 0; k < S; ++k)
 #pragma unroll
-            for (int g = 0; g < NM; ++g) v[g] += upart[((int64_t)(k * NM + g) * B + tok) * ld + item];
+        for (int k = 0; k < UP_FINISH_MAX_S; ++k)
+            if (k < S)
+#pragma unroll
+                for (int g = 0; g < NM; ++g) v[g] += p[k][g];
+        if (item + stride < T) load(item + stride);
         float hv;
         if (ACT == RELU) {
             hv = v[0] > 0.0f ? v[0] : 0.0f;
