@@ -103,6 +103,17 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
     const int lane = tid & (WAVE - 1);
     const int wv = tid / WAVE;
     const int nch = a.d / EPC;                         // 16-byte (code) chunks of a row
+    // The chunk of a row that this thread takes in the up (and gate) dot
+    // products, and the one it accumulates in the down projection.  With one
+    // chunk per thread and fewer chunks than threads, the down chunks go first
+    // to the threads that hold no up chunk: at d = 12288 (Q4_0, 384 chunks)
+    // waves 0-3 take both, 4-5 up only and 6-7 down only, so each SIMD carries
+    // three of the row's 768 chunk units instead of four on two of them.
+    auto up_chunk = [&](int k) { return tid + FT * k; };
+    auto down_chunk = [&](int k) {
+        if constexpr (NC == 1) return tid >= nch ? tid - nch : tid + (FT - nch);
+        return tid + FT * k;
+    };
 
     // Prologue, one memory round trip: this thread's share of x and its run of
     // mask words are loaded before anything waits on either (x first, so the
@@ -284,10 +295,10 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                     const int64_t rbase = (int64_t)max(R.row[g], 0) * a.rb;
 #pragma unroll
                     for (int k = 0; k < NC; ++k) {
-                        const int c = min(tid + FT * k, nch - 1);
-                        R.wu[g][k] = ld16_stream(wup + rbase + 16 * (int64_t)c);
-                        if (ACT == REGLU) R.wg[g][k] = ld16_stream(wgt + rbase + 16 * (int64_t)c);
-                        R.wd[g][k] = ld16_stream(wdn + rbase + 16 * (int64_t)c);
+                        const int cu = min(up_chunk(k), nch - 1), cd = min(down_chunk(k), nch - 1);
+                        R.wu[g][k] = ld16_stream(wup + rbase + 16 * (int64_t)cu);
+                        if (ACT == REGLU) R.wg[g][k] = ld16_stream(wgt + rbase + 16 * (int64_t)cu);
+                        R.wd[g][k] = ld16_stream(wdn + rbase + 16 * (int64_t)cd);
                     }
                 }
                 if (WT == Q4) {
@@ -296,11 +307,11 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         const int64_t sbase = (int64_t)max(R.row[g], 0) * a.rb + a.d / 2;
 #pragma unroll
                         for (int k = 0; k < NC; ++k) {
-                            const int c = min(tid + FT * k, nch - 1);
-                            R.su[g][k] = *(const uint16_t*)(wup + sbase + 2 * c);
+                            const int cu = min(up_chunk(k), nch - 1), cd = min(down_chunk(k), nch - 1);
+                            R.su[g][k] = *(const uint16_t*)(wup + sbase + 2 * cu);
                             if (ACT == REGLU)
-                                R.sg[g][k] = *(const uint16_t*)(wgt + sbase + 2 * c);
-                            R.sd[g][k] = *(const uint16_t*)(wdn + sbase + 2 * c);
+                                R.sg[g][k] = *(const uint16_t*)(wgt + sbase + 2 * cu);
+                            R.sd[g][k] = *(const uint16_t*)(wdn + sbase + 2 * cd);
                         }
                     }
                 }
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         float pu = 0.0f, pg = 0.0f;
 #pragma unroll
                         for (int k = 0; k < NC; ++k) {
-                            const int c = tid + FT * k;
+                            const int c = up_chunk(k);
                             if (c < nch) {
                                 const uint8_t* xp = s_x + b * xrow + (int64_t)c * EPC * XB;
                                 pu = Dot<WT, XT>::run(R.wu[g][k], WT == Q4 ? half_f(R.su[g][k]) : 0.f, xp, pu);
@@ -360,6 +371,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
                         if (r < 0 || b >= nb) hv = 0.0f;
 #pragma unroll
                         for (int k = 0; k < NC; ++k) {
+                            if (down_chunk(k) >= nch) continue;   // no down chunk (whole waves)
                             // a slot that holds no row read row 0 of the partition
                             // (clamped, unconditional loads): its weights are replaced by
                             // zeros here, where they are consumed, so a non-finite value
@@ -415,7 +427,7 @@ __global__ __launch_bounds__(FT) void k_ffn(FfnArgs a, DownOut o) {
             if (b < nb) {
 #pragma unroll
                 for (int k = 0; k < NC; ++k) {
-                    const int c = tid + FT * k;
+                    const int c = down_chunk(k);
                     if (c < nch) {
                         if (WT == Q4) {                // the codes' offset of 8: -8 * sum of h * scale
 #pragma unroll
