@@ -155,6 +155,26 @@ def test_small_parity(name, B):
         log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
 
 
+@pytest.mark.parametrize("base,d", [("opt-fp32", 1216), ("opt30b-fp16", 2368),
+                                    ("llama70b-reglu-fp16", 2368), ("opt175b-q4_0", 9472),
+                                    ("opt175b-q4_0", 16384)])
+def test_fused_kernel_chunk_maps(base, d):
+    """Batch-1 fused kernel with one 16-byte chunk per thread and between 256 and 512
+    chunks per row: the down chunks start at the threads without an up chunk, so
+    threads [0, 2 nch - 512) take both, [2 nch - 512, nch) up only and [nch, 512)
+    down only.  d gives nch = 304 (f32), 296 (f16 and Q4_0): the boundaries fall
+    inside waves; d = 16384 (Q4_0) gives 512 chunks, both on every thread."""
+    wl = S.WORKLOADS[base].scaled(d=d, n=733, r=32, hot_frac=None)
+    log(f"fused chunk map {base} d={d}")
+    L = S.make_layer(wl)
+    dl = DeviceLayer.upload(L, DEV)
+    buf = StepBuffers(dl, 1, DEV)
+    for step in range(3):
+        x = S.make_x(wl, 0, step, 1)
+        e, namb, na = check_step(L, wl.n, x, run_step(dl, buf, x, fused=(step != 1)))
+        log(f"  step {step}: active {na}, ambiguous {namb}, err {e:.2e}")
+
+
 def test_gathered_path_with_more_than_64k_of_lds():
     """f32 weights at batch 6 take the gathered two-kernel path; at d = 2048 the
     token group of x (8 x 2048 fp32 = 64 KiB) plus the mask words and their scan
