@@ -143,7 +143,10 @@ size_t ws_h_bytes(int n, int B) {
 constexpr int UP_SPLIT_SMALL_B = 4;
 constexpr int UP_SPLIT_MAX_B = 16;
 static_assert(UP_SPLIT_SMALL_B <= UP_FINISH_MAX_S, "k_up_finish holds at most UP_FINISH_MAX_S slices");
-int up_split_want(int B, int wt) { return wt == Q4 && B <= UP_SPLIT_MAX_B ? UP_SPLIT_SMALL_B : 1; }
+int up_split_want(int B, int wt) {
+    if (wt != Q4 || B > UP_SPLIT_MAX_B) return 1;
+    return B <= 12 ? UP_SPLIT_SMALL_B : 2;
+}
 int64_t up_part_ld(int n) { return (int64_t)(n + 63) / 64 * 64; }
 
 // the partials of y (down kernels), which the split up kernel's partials share

@@ -345,6 +345,34 @@ __device__ __forceinline__ int kth_active(const uint64_t* s_words, const int* s_
     return 64 * lo + select_bit(s_words[lo], k - s_scan[lo]);
 }
 
+// An argument of the partition `part` (0 hot, 1 cold) when part varies across
+// lanes: a select between the two values, which come from the argument segment
+// through scalar loads.  Indexing the argument's array with a per-lane index
+// instead loads the element with a vector load and waits for it at each use
+// (in the matrix-core up kernel's list emission that was one memory round trip
+// per emitted entry: 14-24 us of a 47 us kernel at batch 8).
+// (pointers pass through readfirstlane, a register value: a plain select of the
+// two loaded pointers is folded back by the compiler into a load of the
+// selected argument address)
+template <typename T>
+__device__ __forceinline__ T* scalar_ptr(T* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    // through a global-address-space pointer, so accesses stay global (not flat)
+    typedef __attribute__((address_space(1))) T GT;
+    return (T*)reinterpret_cast<GT*>(((uint64_t)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ T* by_part(T* const (&v)[2], int part) {
+    T* const p0 = scalar_ptr(v[0]);
+    T* const p1 = scalar_ptr(v[1]);
+    return part == 0 ? p0 : p1;
+}
+__device__ __forceinline__ int by_part(const int (&v)[2], int part) {
+    return part == 0 ? v[0] : v[1];
+}
+
 // Whether a predicted set of T active neurons is computed densely (every row).
 __device__ __forceinline__ bool crosses_to_dense(const FfnArgs& a, int T) {
     return a.dense_from > 0 && T >= a.dense_from;
@@ -458,17 +486,17 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
                 const int id = kth_active(s_words, s_scan, words, item);
                 part = id < a.rows[0] ? 0 : 1;
                 row = part == 0 ? id : id - a.rows[0];
-                if (lane == 0 && b0 == 0) a.out_idx[part][part == 0 ? item : item - H] = row;
+                if (lane == 0 && b0 == 0) by_part(a.out_idx, part)[part == 0 ? item : item - H] = row;
             } else {
                 item_row(a, item, H, dense, part, row);
             }
-            if ((unsigned)row >= (unsigned)a.rows[part]) {     // id outside the partition: h = 0
+            if ((unsigned)row >= (unsigned)by_part(a.rows, part)) {     // id outside the partition: h = 0
                 if (lane == 0)
                     for (int b = 0; b < nb; ++b) a.h[(int64_t)(b0 + b) * a.h_ld + item] = 0.0f;
                 continue;
             }
-            const uint8_t* wu = a.up[part] + (int64_t)row * a.rb;
-            const uint8_t* wg = ACT == REGLU ? a.gate[part] + (int64_t)row * a.rb : nullptr;
+            const uint8_t* wu = by_part(a.up, part) + (int64_t)row * a.rb;
+            const uint8_t* wg = ACT == REGLU ? by_part(a.gate, part) + (int64_t)row * a.rb : nullptr;
             float au[BT], ag[BT];
 #pragma unroll
             for (int b = 0; b < BT; ++b) au[b] = ag[b] = 0.0f;
@@ -511,7 +539,8 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
                 float up = wave_sum(au[b]);
                 float g = ACT == REGLU ? wave_sum(ag[b]) : 0.0f;
                 if (lane == 0 && b < nb) {
-                    up += a.bup[part] ? a.bup[part][row] : 0.0f;
+                    const float* pbu = by_part(a.bup, part);
+                    up += pbu ? pbu[row] : 0.0f;
                     float hv;
                     if (ACT == RELU) {
                         hv = up > 0.0f ? up : 0.0f;
@@ -519,7 +548,8 @@ __global__ __launch_bounds__(THREADS) void k_up(FfnArgs a) {
                         const float r = up > 0.0f ? up : 0.0f;
                         hv = r * r;
                     } else {
-                        g += a.bgate[part] ? a.bgate[part][row] : 0.0f;
+                        const float* pbg = by_part(a.bgate, part);
+                        g += pbg ? pbg[row] : 0.0f;
                         hv = (g > 0.0f ? g : 0.0f) * up;
                     }
                     a.h[(int64_t)(b0 + b) * a.h_ld + item] = hv;

@@ -276,10 +276,10 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
                     const int part = rank < H ? 0 : 1;
                     const int row = part == 0 ? id : id - nhot;
                     if (!dense) {
-                        s_row[rank - i0] = (unsigned)row < (unsigned)a.rows[part] ? row : -1;
+                        s_row[rank - i0] = (unsigned)row < (unsigned)by_part(a.rows, part) ? row : -1;
                         s_part[rank - i0] = part;
                     }
-                    if (lists_out) a.out_idx[part][part == 0 ? rank : rank - H] = row;
+                    if (lists_out) by_part(a.out_idx, part)[part == 0 ? rank : rank - H] = row;
                 }
             }
             r0 += pc;
@@ -298,7 +298,7 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
             const int item = min(i0 + tid, H + C - 1);
             int part, row;
             item_row(a, item, H, dense, part, row);
-            if ((unsigned)row >= (unsigned)a.rows[part]) row = -1;
+            if ((unsigned)row >= (unsigned)by_part(a.rows, part)) row = -1;
             s_row[tid] = i0 + tid < H + C ? row : -1;
             s_part[tid] = part;
         }
@@ -336,8 +336,10 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a,
         const int item = i0 + r;
         if (item < T) {
             const int hp = h_pos(item, H);
-            const float bu = (row >= 0 && a.bup[part]) ? a.bup[part][row] : 0.0f;
-            const float bg = (ACT == REGLU && row >= 0 && a.bgate[part]) ? a.bgate[part][row] : 0.0f;
+            const float* pbu = by_part(a.bup, part);
+            const float* pbg = by_part(a.bgate, part);
+            const float bu = (row >= 0 && pbu) ? pbu[row] : 0.0f;
+            const float bg = (ACT == REGLU && row >= 0 && pbg) ? pbg[row] : 0.0f;
 #pragma unroll
             for (int mt = 0; mt < WT_::MW; ++mt) {
 #pragma unroll
@@ -380,8 +382,10 @@ __device__ __forceinline__ void up_partials(const FfnArgs& a,
         const int item = i0 + r;
         if (item < T) {
             float bias[NM];
-            bias[0] = (slice == 0 && row >= 0 && a.bup[part]) ? a.bup[part][row] : 0.0f;
-            if (NM == 2) bias[NM - 1] = (slice == 0 && row >= 0 && a.bgate[part]) ? a.bgate[part][row] : 0.0f;
+            const float* pbu = by_part(a.bup, part);
+            const float* pbg = by_part(a.bgate, part);
+            bias[0] = (slice == 0 && row >= 0 && pbu) ? pbu[row] : 0.0f;
+            if (NM == 2) bias[NM - 1] = (slice == 0 && row >= 0 && pbg) ? pbg[row] : 0.0f;
 #pragma unroll
             for (int g = 0; g < NM; ++g)
 #pragma unroll
