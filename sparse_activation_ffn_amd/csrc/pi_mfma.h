@@ -242,6 +242,16 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
             T += s_wtot[w];
         }
         const int run0 = before + inc - tot;              // rank of this thread's first set bit
+        // rank of the first set bit of each word (this thread's words), for the
+        // search below
+        int* const s_scan = reinterpret_cast<int*>(s_words + words);
+        {
+            int rr = run0;
+            for (int w = w0; w < min(words, w0 + per); ++w) {
+                s_scan[w] = rr;
+                rr += __popcll(s_words[w]);
+            }
+        }
         const int nhot = a.rows[0];
         const int wh = nhot / 64;
         if (nhot >= a.n) {
@@ -261,28 +271,20 @@ __device__ bool up_resolve(const FfnArgs& a, int i0, int* s_row, int* s_part, ui
         }
         dense = crosses_to_dense(a, T);
         // the set bits of ranks [i0, i0 + UR): this workgroup's list entries and,
-        // unless the step crosses to dense, its items
-        const int ge = min(T, i0 + UR);
-        int r0 = run0;
-        for (int w = w0; w < min(words, w0 + per); ++w) {
-            uint64_t v = s_words[w];
-            const int pc = __popcll(v);
-            if (pc > 0 && r0 < ge && r0 + pc > i0) {
-                const int skip = max(0, i0 - r0);
-                if (skip > 0) v &= ~((1ull << select_bit(v, skip)) - 1ull);
-                for (int rank = r0 + skip; v != 0 && rank < ge; ++rank) {
-                    const int id = 64 * w + __builtin_ctzll(v);
-                    v &= v - 1ull;
-                    const int part = rank < H ? 0 : 1;
-                    const int row = part == 0 ? id : id - nhot;
-                    if (!dense) {
-                        s_row[rank - i0] = (unsigned)row < (unsigned)by_part(a.rows, part) ? row : -1;
-                        s_part[rank - i0] = part;
-                    }
-                    if (lists_out) by_part(a.out_idx, part)[part == 0 ? rank : rank - H] = row;
-                }
+        // unless the step crosses to dense, its items.  Thread t < UR finds the
+        // bit of rank i0 + t by a binary search over the words' first ranks (a
+        // serial walk by the threads owning the words took one entry per
+        // iteration on a few lanes: 7-10 us of the prologue at batch 8)
+        if (tid < UR && i0 + tid < T) {
+            const int rank = i0 + tid;
+            const int id = kth_active(s_words, s_scan, words, rank);
+            const int part = rank < H ? 0 : 1;
+            const int row = part == 0 ? id : id - nhot;
+            if (!dense) {
+                s_row[tid] = (unsigned)row < (unsigned)by_part(a.rows, part) ? row : -1;
+                s_part[tid] = part;
             }
-            r0 += pc;
+            if (lists_out) by_part(a.out_idx, part)[part == 0 ? rank : rank - H] = row;
         }
         if (dense) {
             H = a.rows[0];
