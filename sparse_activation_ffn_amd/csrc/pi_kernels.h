@@ -349,8 +349,8 @@ __device__ __forceinline__ int kth_active(const uint64_t* s_words, const int* s_
 // lanes: a select between the two values, which come from the argument segment
 // through scalar loads.  Indexing the argument's array with a per-lane index
 // instead loads the element with a vector load and waits for it at each use
-// (in the matrix-core up kernel's list emission that was one memory round trip
-// per emitted entry: 14-24 us of a 47 us kernel at batch 8).
+// (in the matrix-core up kernel's list emission, one memory round trip per
+// emitted entry).
 // (pointers pass through readfirstlane, a register value: a plain select of the
 // two loaded pointers is folded back by the compiler into a load of the
 // selected argument address)
