@@ -5,8 +5,10 @@ One step = one pass of the whole hot path over one token batch: predictor
 `pi_sparse_ffn_split` with the mask: compaction into hot/cold lists fused into
 the fused FFN kernel (up/gate, activation and down over the hot and the cold
 partition, one partial of y per workgroup), and the merge fused into the
-reduction of those partials.  Four kernels at batch 1 (five on the
-matrix-core path), no host synchronisation.
+reduction of those partials.  Four kernels at batch 1; six on the
+matrix-core path at batch 2..64 (two predictor kernels and the slice sum, the
+up and down kernels, the reduction), seven where the Q4_0 up kernel is split
+over K; no host synchronisation.
 
 Default workload: the OPT-30B-shaped ReLU layer (d_model 7168, d_ffn 28672,
 predictor rank 1024, fp16 weights, fp32 accumulation, batch 1), hot partition
@@ -24,7 +26,8 @@ kernel against the 8 TB/s HBM peak and against the attainable read rate of a
 plain read stream of the same size (`pi_stream_read`), the dense FFN of the
 same layer, the literal bias-free predictor as a secondary row, the
 Falcon-40B-shaped 60-layer stack (tokens/s of the FFN stack, default run
-only), and the CPU oracle timed on one host core and on all of them.
+only), and the CPU oracle timed on all host cores and on one (the one-core leg
+is skipped where a single step would take over a minute).
 """
 from __future__ import annotations
 
