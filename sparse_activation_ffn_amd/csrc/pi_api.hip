@@ -141,15 +141,17 @@ size_t ws_h_bytes(int n, int B) {
 // fill the chip; 315 -> 323 us with two slices) nor for f16 weights at batch 4
 // (ReGLU-70B-shaped layer 132 -> 139 us), so those run unsplit.
 constexpr int UP_SPLIT_SMALL_B = 4;
-constexpr int UP_SPLIT_MAX_B = 16;
+constexpr int UP_SPLIT_MAX_B = 32;
 static_assert(UP_SPLIT_SMALL_B <= UP_FINISH_MAX_S, "k_up_finish holds at most UP_FINISH_MAX_S slices");
-// K slices of the Q4_0 up kernel at small batches (measured on the OPT-175B
-// Q4_0 layer: two slices beat four from 4 to 14 tokens, e.g. up 44 -> 40 us at
-// batch 8 and 52 -> 42 us at batch 12; four beat two at 16 tokens, 62.5 against
-// 69.4 us)
+// K slices of the Q4_0 up kernel (measured on the OPT-175B Q4_0 layer: two
+// slices beat four from 4 to 14 tokens, e.g. up 44 -> 40 us at batch 8 and
+// 52 -> 42 us at batch 12; four beat two at 16 tokens, 62.5 against 69.4 us;
+// with 17..32 tokens two slices beat none, step 191.5 -> 179.7 us at batch 24
+// and 204.7 -> 193.3 us at batch 32; with 64 tokens none is best, 282 against
+// 296.6 us)
 int up_split_want(int B, int wt) {
     if (wt != Q4 || B > UP_SPLIT_MAX_B) return 1;
-    return B <= 14 ? 2 : UP_SPLIT_SMALL_B;
+    return B == 15 || B == 16 ? UP_SPLIT_SMALL_B : 2;
 }
 int64_t up_part_ld(int n) { return (int64_t)(n + 63) / 64 * 64; }
 
