@@ -227,11 +227,13 @@ MFMA_SMALL = {
 
 @pytest.mark.parametrize("name,B", [("relu-f16-split", 2), ("reglu-f16", 3), ("q4_0", 5),
                                     ("reglu-f16", 16), ("reglu-f16", 33), ("relu-f16-split", 64),
-                                    ("q4_0", 20), ("q4_0", 64), ("q4_0-reglu-split", 48)])
+                                    ("q4_0", 16), ("q4_0", 20), ("q4_0", 32), ("q4_0", 64),
+                                    ("q4_0-reglu-split", 48)])
 def test_matrix_core_batches(name, B):
-    """Batches of 2..64 tokens (matrix-core path: token tiles of 16, 32 and 64): union
-    active set, f16-rounded h and dequantised weights, checked to the fp16 / Q4_0
-    tolerance."""
+    """Batches of 2..64 tokens (matrix-core path: token tiles of 16, 32 and 64; the
+    Q4_0 up kernel in two K slices at 5, 20 and 32 tokens, four at 16, one at 64):
+    union active set, f16-rounded h and dequantised weights, checked to the fp16 /
+    Q4_0 tolerance."""
     wl = MFMA_SMALL[name]
     log(f"matrix-core {name} B={B}")
     L = S.make_layer(wl)
